@@ -1,0 +1,171 @@
+"""Python binding of libattn.so, the gfx950 attention library (decode + prefill).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in include/attn.h. The functions here take
+torch tensors (device memory allocated by the caller), check dtypes, shapes and
+contiguity, and pass raw pointers and sizes. Nothing is allocated here, and
+there is no fallback: if libattn.so is missing or fails to load, every call
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+from .build import LIB_PATH
+
+ATTN_OK = 0
+ATTN_ERR_INVALID = -1
+ATTN_ERR_UNSUPPORTED = -2
+ATTN_ERR_MISALIGNED = -3
+ATTN_ERR_WORKSPACE = -4
+ATTN_ERR_LAUNCH = -5
+ATTN_ERR_DEVICE = -6
+ATTN_MAX_SPLITS = 64
+ATTN_SPLIT_QUANTUM = 128
+
+# Every symbol include/attn.h declares.
+EXPORTS = ("attn_decode_plan", "attn_decode_workspace_size", "attn_decode", "attn_decode_ex",
+           "attn_fwd", "attn_status_string", "attn_version")
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+def lib() -> ctypes.CDLL:
+    """Load libattn.so once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"libattn.so not built at {LIB_PATH}; run attention_attn_decode_amd.build.build()")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    L.attn_decode_plan.argtypes = [i32, i32, i32, i32, i32, i32, i32,
+                                   ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    L.attn_decode_plan.restype = i32
+    L.attn_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+    L.attn_decode_workspace_size.restype = sz
+    dec = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, sz, vp]
+    L.attn_decode.argtypes = dec
+    L.attn_decode.restype = i32
+    L.attn_decode_ex.argtypes = dec + [i32]
+    L.attn_decode_ex.restype = i32
+    L.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp]
+    L.attn_fwd.restype = i32
+    L.attn_status_string.argtypes = [i32]
+    L.attn_status_string.restype = ctypes.c_char_p
+    L.attn_version.argtypes = []
+    L.attn_version.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return lib().attn_status_string(int(status)).decode()
+
+
+def version() -> str:
+    return lib().attn_version().decode()
+
+
+def attn_decode_plan(batch, n_q_heads, n_kv_heads, d, seqlen_q, max_seqlen_k, num_splits=0):
+    """(n_split, chunk) of the decode split plan (host-only)."""
+    ns, ch = ctypes.c_int(0), ctypes.c_int(0)
+    st = lib().attn_decode_plan(batch, n_q_heads, n_kv_heads, d, seqlen_q, max_seqlen_k,
+                                num_splits, ctypes.byref(ns), ctypes.byref(ch))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_decode_plan")
+    return ns.value, ch.value
+
+
+def attn_decode_workspace_size(batch, n_q_heads, seqlen_q, d, max_seqlen_k) -> int:
+    return int(lib().attn_decode_workspace_size(batch, n_q_heads, seqlen_q, d, max_seqlen_k))
+
+
+def _stream_ptr(stream):
+    if stream is None:
+        import torch
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(t, name, dtype, ndim=None):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be device memory")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions")
+
+
+def attn_decode(q, k_cache, v_cache, seqlens_k, o, lse=None, workspace=None, num_splits=0,
+                stream=None):
+    """GQA KV-cache decode; sizes are read from the tensor shapes.
+
+    q, o: bf16 [B, sq, Hq, d]; k_cache, v_cache: bf16 [B, S_max, Hkv, d];
+    seqlens_k: int32 [B]; lse: fp32 [B, Hq, sq] or None; workspace: a uint8 (or
+    any) device tensor of at least attn_decode_workspace_size(...) bytes, or
+    None for a single split.
+    """
+    import torch
+    _check(q, "q", torch.bfloat16, 4)
+    _check(k_cache, "k_cache", torch.bfloat16, 4)
+    _check(v_cache, "v_cache", torch.bfloat16, 4)
+    _check(seqlens_k, "seqlens_k", torch.int32, 1)
+    _check(o, "o", torch.bfloat16, 4)
+    B, sq, Hq, d = q.shape
+    _, S, Hkv, dk = k_cache.shape
+    if tuple(v_cache.shape) != tuple(k_cache.shape) or dk != d or k_cache.shape[0] != B:
+        raise ValueError("k_cache/v_cache must be [B, S_max, Hkv, d] matching q")
+    if tuple(o.shape) != tuple(q.shape) or seqlens_k.shape[0] != B:
+        raise ValueError("o must match q and seqlens_k must have B entries")
+    if lse is not None:
+        _check(lse, "lse", torch.float32, 3)
+        if tuple(lse.shape) != (B, Hq, sq):
+            raise ValueError("lse must be [B, Hq, sq]")
+    wbytes = 0
+    if workspace is not None:
+        if not workspace.is_cuda or not workspace.is_contiguous():
+            raise ValueError("workspace must be contiguous device memory")
+        wbytes = workspace.numel() * workspace.element_size()
+    st = lib().attn_decode_ex(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens_k), _ptr(o),
+                              _ptr(lse), Hq, Hkv, d, sq, B, S, _ptr(workspace), wbytes,
+                              _stream_ptr(stream), int(num_splits))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_decode")
+
+
+def attn_fwd(q, k, v, o, lse=None, causal=True, stream=None):
+    """Prefill forward. q, o: bf16 [B, Sq, Hq, d]; k, v: bf16 [B, Sk, Hkv, d]; lse fp32 [B, Hq, Sq]."""
+    import torch
+    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
+        _check(t, nm, torch.bfloat16, 4)
+    B, Sq, Hq, d = q.shape
+    _, Sk, Hkv, dk = k.shape
+    if tuple(v.shape) != tuple(k.shape) or dk != d or k.shape[0] != B or tuple(o.shape) != tuple(q.shape):
+        raise ValueError("shape mismatch among q, k, v, o")
+    if lse is not None:
+        _check(lse, "lse", torch.float32, 3)
+        if tuple(lse.shape) != (B, Hq, Sq):
+            raise ValueError("lse must be [B, Hq, Sq]")
+    st = lib().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), 1 if causal else 0,
+                        B, Sq, Sk, Hq, Hkv, d, _stream_ptr(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd")

@@ -1,0 +1,274 @@
+#!/usr/bin/env python3
+"""Single-GPU benchmark of the attention hot path on MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input:
+  * GQA decode on the headline workload (batch 32, 64 query / 8 KV heads,
+    d = 128, one new token, KV lengths uniform in [1024, 8192]): split-KV
+    kernel + combine, through the C ABI;
+  * causal prefill (batch 2, 32 heads, d = 128, S = 8192) through attn_fwd.
+The headline `value` is decode KV-read bandwidth: algorithmic K+V bytes
+(sum_b L_b * Hkv * 4d) over the measured duration of the decode call, timed
+with HIP events on the stream the kernels run on. Prefill TFLOP/s (exact causal
+FLOPs, 4 d per visible query-key pair) is reported beside it.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published
+DECODE_SOURCES = ["attention_attn_decode_amd/csrc/decode.hip", "attention_attn_decode_amd/csrc/attn_device.h"]
+FWD_SOURCES = ["attention_attn_decode_amd/csrc/fwd.hip", "attention_attn_decode_amd/csrc/attn_device.h"]
+COUNTERS = os.path.join(ROOT, "profiles", "hbm_traffic_counters.json")
+
+
+def source_hash(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def decode_kv_bytes(seqlens, n_kv_heads, d):
+    """Algorithmic K+V bytes of one decode call: every visible key and value row once (bf16)."""
+    return int(sum(int(L) for L in seqlens)) * n_kv_heads * 4 * d
+
+
+def decode_problem_bytes(seqlens, B, Hq, Hkv, d, sq):
+    """Effective problem bytes: Q, K, V and O each counted once."""
+    return decode_kv_bytes(seqlens, Hkv, d) + 2 * (B * sq * Hq * d * 2)
+
+
+def causal_flops(B, H, S, d):
+    """Exact causal forward FLOPs: 2 GEMMs x 2 flop x d per visible (query, key) pair."""
+    return 4 * d * B * H * (S * (S + 1) // 2)
+
+
+def measured_traffic(kernel, src_hash, units):
+    """HBM bytes per launch from stored rocprofv3 FETCH_SIZE/WRITE_SIZE runs, or None if stale."""
+    try:
+        with open(COUNTERS) as f:
+            rec = json.load(f).get(kernel)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_hash") != src_hash:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline_decode(x, d):
+    """Time the fp64 oracle on the decode workload (full workload, one pass)."""
+    import oracle
+    try:
+        ncores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        ncores = os.cpu_count() or 1
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=ncores):
+        t0 = time.perf_counter()
+        reps = 0
+        while True:
+            oracle.attention(x.q, x.k, x.v, x.seqlens, True)
+            reps += 1
+            if time.perf_counter() - t0 > 10.0 or reps >= 5:
+                break
+        dt = (time.perf_counter() - t0) / reps
+    kv = decode_kv_bytes(x.seqlens, x.k.shape[2], d)
+    return {"value": round(kv / dt / 1e9, 3), "unit": "GB/s", "cores": ncores, "kind": "oracle",
+            "sample": f"full decode workload, {reps} pass(es), {dt:.2f} s per pass, numpy fp64"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--num-splits", type=int, default=0, help="decode split override (0 = automatic)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import attention_attn_decode_amd as aa
+    import workloads as wl
+    from attention_attn_decode_amd import build as _build
+
+    if not os.path.exists(_build.LIB_PATH):
+        _build.build()
+    aa.lib()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    props = torch.cuda.get_device_properties(dev)
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    # ---- decode workload (cache at capacity, rows past each sequence end zero) ----
+    dc = wl.DECODE_CONFIGS["c2"]
+    t0 = time.perf_counter()
+    xd = wl.decode_inputs(dc, pad=wl.BF16_ZERO)
+    B, sq, Hq, d = xd.q.shape
+    S, Hkv = xd.k.shape[1], xd.k.shape[2]
+    sets = []
+    q0, k0, v0 = to_dev(xd.q), to_dev(xd.k), to_dev(xd.v)
+    sl = torch.from_numpy(xd.seqlens.copy()).to(dev)
+    # two resident copies (2 x 1 GiB of cache) alternate so no step reads
+    # K/V left in the 256 MB Infinity Cache by the previous one
+    sets.append((q0, k0, v0))
+    sets.append((q0.clone(), k0.clone(), v0.clone()))
+    wsz = aa.attn_decode_workspace_size(B, Hq, sq, d, S)
+    ws = torch.empty(wsz, dtype=torch.uint8, device=dev)
+    od = torch.empty((B, sq, Hq, d), dtype=torch.bfloat16, device=dev)
+    lsed = torch.empty((B, Hq, sq), dtype=torch.float32, device=dev)
+    n_split, chunk = aa.attn_decode_plan(B, Hq, Hkv, d, sq, S, args.num_splits)
+
+    # ---- prefill workload ----
+    run_prefill = not args.no_prefill
+    if run_prefill:
+        pc = wl.PREFILL_CONFIGS["c5"]
+        xp = wl.prefill_inputs(pc)
+        qp, kp, vp = to_dev(xp.q), to_dev(xp.k), to_dev(xp.v)
+        op = torch.empty_like(qp)
+        lsep = torch.empty((pc.batch, pc.n_q_heads, pc.seqlen), dtype=torch.float32, device=dev)
+        del xp
+    setup_s = time.perf_counter() - t0
+
+    stream = torch.cuda.current_stream()
+
+    def step(i, evs=None):
+        q, k, v = sets[i % 2]
+        if evs:
+            evs[0].record(stream)
+        aa.attn_decode(q, k, v, sl, od, lsed, workspace=ws, num_splits=args.num_splits, stream=stream)
+        if evs:
+            evs[1].record(stream)
+        if run_prefill:
+            aa.attn_fwd(qp, kp, vp, op, lsep, causal=True, stream=stream)
+        if evs:
+            evs[2].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(i, events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    dec_ms = [e[0].elapsed_time(e[1]) for e in events]
+    pre_ms = [e[1].elapsed_time(e[2]) for e in events]
+    dec_mean = statistics.fmean(dec_ms)
+    pre_mean = statistics.fmean(pre_ms) if run_prefill else 0.0
+
+    kv_bytes = decode_kv_bytes(xd.seqlens, Hkv, d)
+    dec_gbps = kv_bytes / (dec_mean * 1e-3) / 1e9
+    prob_gbps = decode_problem_bytes(xd.seqlens, B, Hq, Hkv, d, sq) / (dec_mean * 1e-3) / 1e9
+
+    # plain device copy for context: practical HBM rate on this part
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    ce = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ce[0].record(stream)
+    for _ in range(5):
+        dst.copy_(src)
+    ce[1].record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 5 * 2 * src.numel() / (ce[0].elapsed_time(ce[1]) * 1e-3) / 1e9
+    del src, dst
+
+    dec_hash = source_hash(DECODE_SOURCES)
+    result = {
+        "metric": "decode KV-read GB/s (% HBM peak); causal prefill fwd TFLOP/s (% MFMA peak)",
+        "value": round(dec_gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "gqa-decode b=32 hq=64 hkv=8 d=128 sq=1 kv_len~U[1024,8192] (seed 1001)",
+            "global_batch": B,
+            "seq_len": int(S),
+            "kv_tokens": int(xd.seqlens.sum()),
+            "splits": n_split,
+            "chunk": chunk,
+            "prefill_workload": "causal-prefill b=2 h=32 d=128 s=8192 (seed 1004)" if run_prefill else None,
+            "parallelism": "single-gpu",
+            "device": props.name,
+            "cus": props.multi_processor_count,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "attn_decode = decode_split_kv + combine_splits",
+            "achieved": round(dec_gbps, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
+            "traffic": measured_traffic("attn_decode", dec_hash, kv_bytes),
+            "algorithmic_bytes_per_launch": kv_bytes,
+            "avg_launch_ms": round(dec_mean, 5),
+        },
+        "decode": {
+            "ms_mean": round(dec_mean, 5),
+            "ms_median": round(statistics.median(dec_ms), 5),
+            "ms_min": round(min(dec_ms), 5),
+            "kv_read_GBps": round(dec_gbps, 2),
+            "problem_GBps": round(prob_gbps, 2),
+            "frac_hbm_peak": round(dec_gbps / HBM_PEAK_GBPS, 4),
+            "frac_of_device_copy": round(dec_gbps / copy_gbps, 4),
+        },
+        "device_copy_GBps": round(copy_gbps, 1),
+        "setup_s": round(setup_s, 1),
+    }
+    if run_prefill:
+        fl = causal_flops(pc.batch, pc.n_q_heads, pc.seqlen, pc.d)
+        tf = fl / (pre_mean * 1e-3) / 1e12
+        result["prefill"] = {
+            "bound": "mfma",
+            "kernel": "fwd_tile",
+            "ms_mean": round(pre_mean, 5),
+            "ms_median": round(statistics.median(pre_ms), 5),
+            "flops": fl,
+            "achieved": round(tf, 2),
+            "peak": BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+            "traffic": measured_traffic("fwd_tile", source_hash(FWD_SOURCES), None),
+        }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_decode(xd, d)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

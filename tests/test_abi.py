@@ -1,0 +1,119 @@
+"""The C-ABI library: loads, exports every declared symbol, host-only logic.
+
+CPU only: nothing here launches a kernel (validation failures return before
+any device call; planning and workspace sizing are pure host functions).
+"""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import attention_attn_decode_amd as aa
+from tests._libload import ensure_built
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "attn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_]+)\s*\(", text)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    L = ensure_built()
+    names = declared_functions()
+    assert "attn_decode" in names and "attn_fwd" in names
+    for nm in names:
+        assert hasattr(L, nm), f"libattn.so does not export {nm}"
+    assert sorted(aa.EXPORTS) == names
+
+
+def test_status_strings_and_version():
+    ensure_built()
+    for code in (0, -1, -2, -3, -4, -5, -6):
+        s = aa.status_string(code)
+        assert s and s != "unknown status"
+    assert aa.status_string(12345) == "unknown status"
+    assert "gfx950" in aa.version()
+
+
+def _expected_plan(B, Hq, Hkv, d, sq, S, req):
+    cap = min(aa.ATTN_MAX_SPLITS, math.ceil(S / aa.ATTN_SPLIT_QUANTUM))
+    if req > 0:
+        n = req
+    else:
+        n = math.ceil(4096 / (B * Hkv))
+        n = min(n, math.ceil(S / 256))
+    n = max(1, min(n, cap))
+    chunk = math.ceil(math.ceil(S / n) / 128) * 128
+    return math.ceil(S / chunk), chunk
+
+
+@pytest.mark.parametrize("shape", [
+    (1, 8, 1, 64, 1, 512), (32, 64, 8, 128, 1, 8192), (16, 32, 8, 64, 4, 4096),
+    (4, 32, 8, 128, 1, 131072), (3, 4, 4, 128, 1, 1), (2, 16, 1, 64, 1, 1000),
+])
+@pytest.mark.parametrize("req", [0, 1, 2, 7, 64, 1000])
+def test_decode_plan_covers_range_and_respects_limits(shape, req):
+    ensure_built()
+    B, Hq, Hkv, d, sq, S = shape
+    n, chunk = aa.attn_decode_plan(B, Hq, Hkv, d, sq, S, req)
+    assert (n, chunk) == _expected_plan(B, Hq, Hkv, d, sq, S, req)
+    assert 1 <= n <= aa.ATTN_MAX_SPLITS
+    assert chunk % aa.ATTN_SPLIT_QUANTUM == 0
+    assert (n - 1) * chunk < S <= n * chunk  # every split non-empty for a full-length row
+    need = B * Hq * sq * n * (d + 2) * 4
+    assert aa.attn_decode_workspace_size(B, Hq, sq, d, S) >= need
+
+
+def test_auto_plans_of_the_five_workloads():
+    ensure_built()
+    assert aa.attn_decode_plan(1, 8, 1, 64, 1, 512) == (2, 256)
+    assert aa.attn_decode_plan(32, 64, 8, 128, 1, 8192) == (16, 512)
+    assert aa.attn_decode_plan(16, 32, 8, 64, 4, 4096) == (16, 256)
+    assert aa.attn_decode_plan(4, 32, 8, 128, 1, 131072) == (64, 2048)
+
+
+def test_workspace_size_formula():
+    ensure_built()
+    assert aa.attn_decode_workspace_size(4, 32, 1, 128, 131072) == 4 * 32 * 64 * 130 * 4
+    assert aa.attn_decode_workspace_size(1, 8, 1, 64, 100) == 8 * 1 * 66 * 4
+    assert aa.attn_decode_workspace_size(0, 8, 1, 64, 100) == 0
+    assert aa.attn_decode_workspace_size(1, 8, 1, 64, 0) == 0
+
+
+@pytest.mark.parametrize("args,status", [
+    ((32, 8, 128, 1, 1, 64), aa.ATTN_OK),
+    ((30, 8, 128, 1, 1, 64), aa.ATTN_ERR_INVALID),       # Hq % Hkv
+    ((32, 8, 96, 1, 1, 64), aa.ATTN_ERR_UNSUPPORTED),    # d
+    ((32, 8, 128, 5, 1, 64), aa.ATTN_ERR_UNSUPPORTED),   # G * sq = 20 > 16
+    ((16, 1, 64, 1, 1, 64), aa.ATTN_OK),                 # G = 16, the widest group
+    ((32, 8, 128, 0, 1, 64), aa.ATTN_ERR_INVALID),       # sq = 0
+    ((32, 8, 128, 1, 0, 64), aa.ATTN_ERR_INVALID),       # batch = 0
+    ((32, 8, 128, 1, 1, 0), aa.ATTN_ERR_INVALID),        # max_seqlen_k = 0
+])
+def test_plan_validation(args, status):
+    L = ensure_built()
+    Hq, Hkv, d, sq, B, S = args
+    ns, ch = ctypes.c_int(), ctypes.c_int()
+    assert L.attn_decode_plan(B, Hq, Hkv, d, sq, S, 0, ctypes.byref(ns), ctypes.byref(ch)) == status
+
+
+def test_null_pointers_are_rejected_before_any_device_work():
+    L = ensure_built()
+    fake = ctypes.c_void_p(0x1000)
+    assert L.attn_decode(None, fake, fake, fake, fake, None, 8, 1, 64, 1, 1, 16, None, 0, None) == aa.ATTN_ERR_INVALID
+    assert L.attn_decode(fake, fake, fake, None, fake, None, 8, 1, 64, 1, 1, 16, None, 0, None) == aa.ATTN_ERR_INVALID
+    assert L.attn_fwd(fake, None, fake, fake, None, 1, 1, 16, 16, 8, 8, 64, None) == aa.ATTN_ERR_INVALID
+    # shape errors are reported before alignment or launch
+    assert L.attn_fwd(fake, fake, fake, fake, None, 1, 1, 16, 16, 8, 8, 80, None) == aa.ATTN_ERR_UNSUPPORTED
+    assert L.attn_fwd(fake, fake, fake, fake, None, 1, 1, 16, 16, 8, 3, 64, None) == aa.ATTN_ERR_INVALID
+    # misaligned pointers
+    odd = ctypes.c_void_p(0x1002)
+    assert L.attn_decode(odd, fake, fake, fake, fake, None, 8, 1, 64, 1, 1, 16, None, 0, None) == aa.ATTN_ERR_MISALIGNED
+    assert L.attn_fwd(fake, fake, odd, fake, None, 1, 1, 16, 16, 8, 8, 64, None) == aa.ATTN_ERR_MISALIGNED
+    # workspace too small for a multi-split plan
+    assert L.attn_decode_ex(fake, fake, fake, fake, fake, None, 8, 1, 64, 1, 1, 4096, fake, 16, None, 4) == aa.ATTN_ERR_WORKSPACE

@@ -1,0 +1,185 @@
+"""Parity of the HIP decode path (split kernel + combine) with the fp64 oracle.
+
+All calls go through the C ABI (libattn.so) via the ctypes binding.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+from tests import _gpu as G
+from tests._libload import ensure_built
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def aa():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    ensure_built()
+    import attention_attn_decode_amd as mod
+    return mod
+
+
+def run_decode(aa, x, num_splits=0, workspace="auto", poison=True):
+    torch = G.torch()
+    B, sq, Hq, d = x.q.shape
+    S, Hkv = x.k.shape[1], x.k.shape[2]
+    q, k, v = G.dev_bf16(x.q), G.dev_bf16(x.k), G.dev_bf16(x.v)
+    sl = G.dev_i32(x.seqlens)
+    o = G.nan_like_bf16((B, sq, Hq, d)) if poison else torch.empty((B, sq, Hq, d), dtype=torch.bfloat16, device="cuda")
+    lse = G.nan_f32((B, Hq, sq)) if poison else torch.empty((B, Hq, sq), dtype=torch.float32, device="cuda")
+    ws = None
+    if workspace == "auto":
+        nbytes = aa.attn_decode_workspace_size(B, Hq, sq, d, S)
+        ws = torch.full((nbytes // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    aa.attn_decode(q, k, v, sl, o, lse, workspace=ws, num_splits=num_splits)
+    torch.cuda.synchronize()
+    return G.host_f64(o), G.host_f64(lse)
+
+
+def check(aa, x, tag, **kw):
+    O_ref, L_ref = oracle.attention(x.q, x.k, x.v, x.seqlens, True)
+    o, lse = run_decode(aa, x, **kw)
+    return G.assert_parity(o, lse, O_ref, L_ref, tag)
+
+
+@pytest.mark.parametrize("cfg", ["c1", "c3", "c2", "c4"])
+def test_decode_workload_parity(aa, cfg):
+    """Full-size workloads (cache rows past each sequence end are NaN)."""
+    x = wl.decode_inputs(cfg)
+    print(f"[decode parity] {cfg} shape q{x.q.shape} k{x.k.shape}", flush=True)
+    err, scale = check(aa, x, cfg)
+    print(f"[decode parity] {cfg}: max|dO| = {err:.3e} (max|O| {scale:.3e})", flush=True)
+
+
+@pytest.mark.parametrize("num_splits", [1, 2, 3, 5, 16, 64])
+def test_split_count_invariance(aa, num_splits):
+    x = wl.make_decode(3, 16, 4, 64, 2, 2000, [2000, 777, 129], seed=51)
+    check(aa, x, f"splits={num_splits}", num_splits=num_splits)
+
+
+def test_no_workspace_single_split(aa):
+    x = wl.make_decode(2, 32, 8, 128, 1, 3000, [3000, 1234], seed=53)
+    check(aa, x, "no-workspace", workspace=None)
+
+
+def test_bitwise_determinism(aa):
+    x = wl.make_decode(4, 64, 8, 128, 1, 5000, [5000, 4097, 100, 2048], seed=55)
+    a = run_decode(aa, x)
+    b = run_decode(aa, x)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_needles_at_block_and_split_boundaries(aa, d):
+    """Key j* = 8 q (score gap >> 40) must dominate: O = v[j*] for that head."""
+    L, chunk_splits = 700, 3  # chunk 256: split boundaries at 256, 512
+    needles = [0, 1, 31, 32, 63, 127, 128, 255, 256, 257, 511, 512, 699]
+    B = len(needles)
+    x = wl.make_decode(B, 8, 1, d, 1, 768, [L] * B, seed=57 + d)
+    qf = oracle.bf16_bits_to_f64(x.q[:, 0, 0])  # head 0 of each batch row
+    for b, j in enumerate(needles):
+        x.k[b, j, 0] = wl.f32_to_bf16_bits((8.0 * qf[b]).astype(np.float32))
+    o, lse = run_decode(aa, x, num_splits=chunk_splits)
+    for b, j in enumerate(needles):
+        want = oracle.bf16_bits_to_f64(x.v[b, j, 0])
+        assert np.abs(o[b, 0, 0] - want).max() <= 2.0 ** -7 * max(1.0, np.abs(want).max()), f"needle {j}"
+    O_ref, L_ref = oracle.attention(x.q, x.k, x.v, x.seqlens, True)
+    G.assert_parity(o, lse, O_ref, L_ref, "needles")
+
+
+def test_future_needle_is_masked_for_earlier_tokens(aa):
+    """sq = 4: key L-1 is visible only to the last new token (bottom-right)."""
+    L, sq = 1000, 4
+    x = wl.make_decode(1, 4, 1, 64, sq, 1024, [L], seed=59)
+    for t in range(sq):
+        qf = oracle.bf16_bits_to_f64(x.q[0, t, 0])
+        x.k[0, L - 1, 0] = wl.f32_to_bf16_bits((8.0 * qf).astype(np.float32)) if t == 0 else x.k[0, L - 1, 0]
+    o, lse = run_decode(aa, x)
+    vneedle = oracle.bf16_bits_to_f64(x.v[0, L - 1, 0])
+    assert np.abs(o[0, 0, 0] - vneedle).max() > 0.1  # token 0 must not see key L-1
+    O_ref, L_ref = oracle.attention(x.q, x.k, x.v, x.seqlens, True)
+    G.assert_parity(o, lse, O_ref, L_ref, "future-needle")
+
+
+@pytest.mark.parametrize("sq", [1, 4])
+def test_empty_short_and_ragged_sequences(aa, sq):
+    lens = [0, 1, 2, 3, 5, 31, 32, 33, 127, 128, 129, 300]
+    x = wl.make_decode(len(lens), 8, 2, 64, sq, 300, lens, seed=61 + sq)
+    O_ref, L_ref = oracle.attention(x.q, x.k, x.v, x.seqlens, True)
+    for ns in (0, 1, 3):
+        o, lse = run_decode(aa, x, num_splits=ns)
+        G.assert_parity(o, lse, O_ref, L_ref, f"ragged sq={sq} splits={ns}")
+        empty = np.isneginf(L_ref)
+        assert np.all(o[np.transpose(empty, (0, 2, 1))] == 0.0)
+
+
+def test_seqlens_are_clamped_to_capacity(aa):
+    x = wl.make_decode(2, 8, 1, 128, 1, 256, [256, 100], seed=63)
+    O_ref, L_ref = oracle.attention(x.q, x.k, x.v, x.seqlens, True)
+    x.seqlens = np.array([10_000, 100], dtype=np.int32)
+    o, lse = run_decode(aa, x)
+    G.assert_parity(o, lse, O_ref, L_ref, "clamp")
+
+
+@pytest.mark.parametrize("shape", [(16, 1, 1), (8, 2, 4), (4, 4, 4), (1, 1, 1), (2, 1, 8), (32, 2, 1)])
+@pytest.mark.parametrize("d", [64, 128])
+def test_group_shapes(aa, shape, d):
+    """Packed query columns from 1 up to the 16-column maximum, G*sq = 16 included."""
+    Hq, Hkv, sq = shape
+    x = wl.make_decode(2, Hq, Hkv, d, sq, 600, [600, 333], seed=67 + Hq + sq + d)
+    check(aa, x, f"Hq={Hq} Hkv={Hkv} sq={sq} d={d}")
+
+
+def test_hip_graph_replay_without_memset(aa):
+    """Captured decode + combine, replayed with new queries and a reused workspace."""
+    torch = G.torch()
+    x = wl.make_decode(4, 32, 8, 128, 1, 4096, [4096, 3000, 17, 2049], seed=71)
+    B, sq, Hq, d = x.q.shape
+    q, k, v = G.dev_bf16(x.q), G.dev_bf16(x.k), G.dev_bf16(x.v)
+    sl = G.dev_i32(x.seqlens)
+    o = G.nan_like_bf16((B, sq, Hq, d))
+    lse = G.nan_f32((B, Hq, sq))
+    nbytes = aa.attn_decode_workspace_size(B, Hq, sq, d, x.k.shape[1])
+    ws = torch.full((nbytes // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        aa.attn_decode(q, k, v, sl, o, lse, workspace=ws, stream=s)  # warm-up outside capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        aa.attn_decode(q, k, v, sl, o, lse, workspace=ws, stream=s)
+    for rep in range(3):
+        xq = wl.make_decode(B, Hq, 8, d, sq, 4096, x.seqlens, seed=100 + rep)
+        q.copy_(G.dev_bf16(xq.q))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        og, lg = G.host_f64(o), G.host_f64(lse)
+        # eager call on fresh outputs for the same inputs
+        o2 = G.nan_like_bf16((B, sq, Hq, d))
+        l2 = G.nan_f32((B, Hq, sq))
+        aa.attn_decode(q, k, v, sl, o2, l2, workspace=ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(og, G.host_f64(o2)) and np.array_equal(lg, G.host_f64(l2)), f"replay {rep}"
+        O_ref, L_ref = oracle.attention(xq.q, x.k, x.v, x.seqlens, True)
+        G.assert_parity(og, lg, O_ref, L_ref, f"graph replay {rep}")
+
+
+def test_errors_are_reported_without_launch(aa):
+    torch = G.torch()
+    x = wl.make_decode(1, 8, 1, 64, 1, 4096, [4096], seed=73)
+    q, k, v = G.dev_bf16(x.q), G.dev_bf16(x.k), G.dev_bf16(x.v)
+    sl = G.dev_i32(x.seqlens)
+    o = torch.zeros((1, 1, 8, 64), dtype=torch.bfloat16, device="cuda")
+    small = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(aa.AttnError) as e:
+        aa.attn_decode(q, k, v, sl, o, None, workspace=small, num_splits=4)
+    assert e.value.status == aa.ATTN_ERR_WORKSPACE
+    torch.cuda.synchronize()
+    assert float(o.abs().max()) == 0.0  # nothing was written
