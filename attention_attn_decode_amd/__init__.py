@@ -21,8 +21,9 @@ ATTN_ERR_MISALIGNED = -3
 ATTN_ERR_WORKSPACE = -4
 ATTN_ERR_LAUNCH = -5
 ATTN_ERR_DEVICE = -6
-ATTN_MAX_SPLITS = 64
-ATTN_SPLIT_QUANTUM = 128
+ATTN_MAX_PIECES = 4096
+ATTN_MIN_PIECE = 64
+ATTN_MAX_BATCH = 8192
 
 # Every symbol include/attn.h declares.
 EXPORTS = ("attn_decode_plan", "attn_decode_workspace_size", "attn_decode", "attn_decode_ex",
@@ -49,7 +50,7 @@ def lib() -> ctypes.CDLL:
     L.attn_decode_plan.argtypes = [i32, i32, i32, i32, i32, i32, i32,
                                    ctypes.POINTER(i32), ctypes.POINTER(i32)]
     L.attn_decode_plan.restype = i32
-    L.attn_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+    L.attn_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
     L.attn_decode_workspace_size.restype = sz
     dec = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, sz, vp]
     L.attn_decode.argtypes = dec
@@ -75,7 +76,7 @@ def version() -> str:
 
 
 def attn_decode_plan(batch, n_q_heads, n_kv_heads, d, seqlen_q, max_seqlen_k, num_splits=0):
-    """(n_split, chunk) of the decode split plan (host-only)."""
+    """(pieces per KV head, minimum piece length) of the decode plan (host-only)."""
     ns, ch = ctypes.c_int(0), ctypes.c_int(0)
     st = lib().attn_decode_plan(batch, n_q_heads, n_kv_heads, d, seqlen_q, max_seqlen_k,
                                 num_splits, ctypes.byref(ns), ctypes.byref(ch))
@@ -84,8 +85,10 @@ def attn_decode_plan(batch, n_q_heads, n_kv_heads, d, seqlen_q, max_seqlen_k, nu
     return ns.value, ch.value
 
 
-def attn_decode_workspace_size(batch, n_q_heads, seqlen_q, d, max_seqlen_k) -> int:
-    return int(lib().attn_decode_workspace_size(batch, n_q_heads, seqlen_q, d, max_seqlen_k))
+def attn_decode_workspace_size(batch, n_q_heads, n_kv_heads, seqlen_q, d, max_seqlen_k,
+                               num_splits=0) -> int:
+    return int(lib().attn_decode_workspace_size(batch, n_q_heads, n_kv_heads, seqlen_q, d,
+                                                max_seqlen_k, num_splits))
 
 
 def _stream_ptr(stream):
@@ -121,8 +124,8 @@ def attn_decode(q, k_cache, v_cache, seqlens_k, o, lse=None, workspace=None, num
 
     q, o: bf16 [B, sq, Hq, d]; k_cache, v_cache: bf16 [B, S_max, Hkv, d];
     seqlens_k: int32 [B]; lse: fp32 [B, Hq, sq] or None; workspace: a uint8 (or
-    any) device tensor of at least attn_decode_workspace_size(...) bytes, or
-    None for a single split.
+    any) device tensor of at least attn_decode_workspace_size(...) bytes for the
+    same num_splits, or None for one piece per KV head.
     """
     import torch
     _check(q, "q", torch.bfloat16, 4)

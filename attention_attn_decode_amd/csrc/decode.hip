@@ -1,4 +1,4 @@
-// GQA KV-cache decode for gfx950: split-KV kernel and log-sum-exp combine.
+// GQA KV-cache decode for gfx950: balanced split-KV kernel and log-sum-exp combine.
 //
 // Pages cited by title and section:
 //   [FA4-decode] "Optimization diaries: S/P ping-pong for FlashAttention-4 decode"
@@ -6,42 +6,49 @@
 //   [FA4-edges]  "Flash Attention 4 — warp-role choreography and the edges"
 //
 // Operand swap ([GQA-SM100] §Starting with the simple pipeline and the
-// introduction): S^T = K Q^T / sqrt(d) and O^T = V^T P^T, so key positions
-// run along the MFMA's M dimension and the small packed query group (the
-// G = Hq / Hkv heads of one KV head times the seqlen_q new tokens, at most 16)
-// along N. With v_mfma_f32_16x16x32_bf16 a lane then owns one query column:
-// the column max and sum over keys are mostly in-lane, the rescale factor of
-// O^T is one scalar per lane, and P leaves the S^T accumulator already in the
-// layout the P*V MFMA wants as its B operand (it never goes through memory).
+// introduction): S^T = K Q^T / sqrt(d) and O^T = V^T P^T, so key positions run
+// along the MFMA's M dimension and the small packed query group (the G = Hq/Hkv
+// heads of one KV head times the seqlen_q new tokens, at most 16) along N. With
+// v_mfma_f32_16x16x32_bf16 a lane then owns one query column: the column max and
+// sum over keys are mostly in-lane, the rescale factor of O^T is one scalar per
+// lane, and P leaves the S^T accumulator already in the layout the P*V MFMA
+// wants as its B operand (it never goes through memory).
 //
-// Work decomposition: one work-group of four waves per (split, kv head, batch).
-// The split's key range is cut into 32-position sub-blocks dealt round-robin to
-// the waves; each wave streams its own sub-blocks (no cross-wave barrier in the
-// loop) with register double buffering: the loads of sub-block i+1 are issued
-// before the MFMA/softmax work of sub-block i. K and V pass through a per-wave
-// LDS tile that changes their layout: K row-major with an XOR swizzle of its
-// 16-byte chunks, V transposed (d-major) so the P*V A operand is one 16-byte
-// LDS read. At the end the four waves merge their (max, sum, O^T) through LDS
-// and the work-group writes one split partial (or, with a single split, the
-// final O and LSE).
+// Splitting ([GQA-SM100] §Combining the KV splits: splits give a small batch
+// enough parallel work; each returns an unnormalised output, its maximum and
+// its denominator). Here the split is balanced on the device: for each KV head
+// the keys of all sequences are laid end to end (sequence b occupies flattened
+// positions [start_b, start_b + L_b)), and that range is cut into P_eff equal
+// pieces. Each wave is an independent worker owning one (piece, KV head) pair,
+// so ragged lengths cost nothing in balance and there are no empty work-groups.
+// A piece may cross sequence boundaries; the wave then emits one partial per
+// sequence segment it covered. The partial of piece w for sequence b goes to
+// slot w + b of its KV head: pieces are contiguous and ordered, so (w, b) ->
+// w + b is one-to-one, and P + B slots per head always suffice.
+//
+// Streaming: one work-group of four independent waves per CU. Each wave keeps
+// two sub-blocks of 32 keys in flight in a two-slot register ring (nontemporal
+// 16-byte loads; K and V are read exactly once) and, per sub-block, passes K and V
+// through a private LDS tile that changes their layout: K row-major with an
+// XOR swizzle of its 16-byte chunks, V transposed (d-major) so the P*V A
+// operand is one 16-byte LDS read. There is no work-group barrier.
 //
 // Key order inside a sub-block: MFMA row i of score tile t (0/1) holds key
 // 8 * (i / 4) + 4 * t + (i % 4). Lane group g (= lane / 16) then receives the
 // scores of keys 8g .. 8g + 7 in its two accumulators, exactly the eight
-// contiguous keys its P*V B-operand slots need, so the V^T read is contiguous.
+// contiguous keys its P*V B-operand slots need.
 #include "attn_device.h"
 
 namespace attn {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kSub = 32;  // key positions per wave sub-block
-constexpr int kCols = 16; // packed query columns per work-group
+constexpr int kWaves = 4;  // waves (independent workers) per work-group
+constexpr int kSub = 32;   // keys per sub-block
+constexpr int kCols = 16;  // packed query columns
+constexpr int kMaxBatch = 8192;  // sequences per call (lengths staged in LDS)
 
-// XOR swizzle of the 16-byte chunk index of K row r in LDS (row-major [32][D]).
-// For D = 128 (16 chunks per 256-byte row) and D = 64 (8 chunks per 128-byte
-// row) it makes the 16 rows one QK A-operand read touches land on 16 distinct
-// 16-byte bank groups.
+// XOR swizzle of the 16-byte chunk index of K row r in the LDS tile [32][D]:
+// the 16 rows one QK A-operand read touches land on 16 distinct bank groups.
 template <int D>
 __device__ __forceinline__ int k_swz(int r) {
   if constexpr (D == 128) {
@@ -52,101 +59,180 @@ __device__ __forceinline__ int k_swz(int r) {
   }
 }
 
-// Swizzle of the 8-key unit of V^T row dd in LDS (d-major [D][32]).
+// Swizzle of the 8-key unit of V^T row dd in the LDS tile [D][32].
 __device__ __forceinline__ int vt_swz(int dd) { return (dd >> 2) & 3; }
 
+__device__ __forceinline__ int clamp_len(int L, int max_len) {
+  return L < 0 ? 0 : (L > max_len ? max_len : L);
+}
+
+__device__ __forceinline__ uint4 ld_stream(const uint16_t *p) {
+  typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+  const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+  return make_uint4(t[0], t[1], t[2], t[3]);
+}
+
+// Sum over all sequences of the (clamped) lengths in `lens` (every lane gets it).
+__device__ long long total_keys(const int *lens, int B) {
+  const int lane = threadIdx.x & 63;
+  long long t = 0;
+  for (int b = lane; b < B; b += 64) t += lens[b];
+  for (int m = 1; m < 64; m <<= 1) t += __shfl_xor(t, m, 64);
+  return t;
+}
+
+// Number of pieces per KV head: the requested P, but no piece shorter than
+// min_piece keys (so tiny inputs do not fan out into empty work).
+__device__ __forceinline__ int pieces_for(long long T, int P, int min_piece) {
+  const long long by_len = (T + min_piece - 1) / min_piece;
+  return (int)(by_len < P ? (by_len < 1 ? 1 : by_len) : P);
+}
+
+// Piece w of P_eff covers flattened keys [w*T/P_eff, (w+1)*T/P_eff); the piece
+// holding flattened key x is ((x + 1) * P_eff - 1) / T.
+__device__ __forceinline__ long long piece_begin(int w, long long T, int P_eff) {
+  return (long long)w * T / P_eff;
+}
+__device__ __forceinline__ int piece_of(long long x, long long T, int P_eff) {
+  return (int)(((x + 1) * P_eff - 1) / T);
+}
+
+struct Seg {
+  int b;            // sequence
+  int lo, hi;       // local key range [lo, hi) of this segment
+  int L;            // clamped sequence length
+  long long start;  // flattened start of the sequence
+};
+
+// The sequence containing flattened key x (x < total): wave-wide scan over the
+// clamped lengths, 64 sequences at a time.
+__device__ Seg find_segment(const int *lens, int B, long long x, long long r1) {
+  const int lane = threadIdx.x & 63;
+  long long carry = 0;
+  for (int base = 0; base < B; base += 64) {
+    const int b = base + lane;
+    const int L = b < B ? lens[b] : 0;
+    long long incl = L;
+    for (int off = 1; off < 64; off <<= 1) {
+      const long long y = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += y;
+    }
+    const long long st = carry + incl - L;
+    const unsigned long long hit = __ballot(L > 0 && st <= x && x < st + L);
+    if (hit) {
+      const int h = __ffsll((long long)hit) - 1;
+      Seg s;
+      s.b = base + h;
+      s.start = __shfl(st, h, 64);
+      s.L = __shfl(L, h, 64);
+      s.lo = (int)(x - s.start);
+      const long long e = r1 - s.start;
+      s.hi = (int)(e < s.L ? e : s.L);
+      return s;
+    }
+    carry += __shfl(incl, 63, 64);
+  }
+  Seg none = {B, 0, 0, 0, carry};
+  return none;
+}
+
+// Next non-empty sequence segment before flattened position r1.
+__device__ bool next_segment(Seg &s, const int *lens, int B, long long r1) {
+  long long st = s.start + s.L;
+  for (int b = s.b + 1; b < B && st < r1; ++b) {
+    const int L = lens[b];
+    if (L > 0) {
+      s.b = b;
+      s.start = st;
+      s.L = L;
+      s.lo = 0;
+      const long long e = r1 - st;
+      s.hi = (int)(e < L ? e : L);
+      return true;
+    }
+  }
+  return false;
+}
+
 template <int D>
-struct DecodeSmem {
-  static constexpr int kTile = kSub * D;                      // bf16 elements per K or V^T tile
-  static constexpr int kLoopBytes = kWaves * 2 * kTile * 2;   // K + V^T per wave
-  static constexpr int kMergeBytes = kWaves * kCols * (D + 2) * 4;
-  static constexpr int kBytes = kLoopBytes > kMergeBytes ? kLoopBytes : kMergeBytes;
+struct Slot {
+  static constexpr int CH = D / 8;
+  static constexpr int RPI = 64 / CH;    // rows one wave-wide 16-byte load covers
+  static constexpr int NK = kSub / RPI;  // K loads per lane
+  static constexpr int NVG = CH / 8;     // 4-row V groups per lane
+  static constexpr int KST = D / 32;     // QK k-steps
+  uint4 k[NK];
+  uint4 v[NVG][4];
+  uint4 q[KST];
 };
 
 template <int D>
-__global__ void __launch_bounds__(256, 2)
-decode_split_kv(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
-                const uint16_t *__restrict__ vc, const int *__restrict__ seqlens,
-                uint16_t *__restrict__ o, float *__restrict__ lse, float *__restrict__ ws_o,
-                float2 *__restrict__ ws_ml, int Hq, int Hkv, int sq, int max_len, int chunk,
-                int n_split, float scale_log2) {
-  constexpr int CH = D / 8;       // 16-byte chunks per row
-  constexpr int RPI = 64 / CH;    // rows one wave-wide 16-byte load covers
-  constexpr int NK = kSub / RPI;  // K loads per lane per sub-block
-  constexpr int NVG = CH / 8;     // 4-row V groups per lane per sub-block
-  constexpr int KST = D / 32;     // k-steps of the QK MFMA
-  constexpr int MT = D / 16;      // row tiles of O^T
-  __shared__ __attribute__((aligned(16))) unsigned char smem[DecodeSmem<D>::kBytes];
+__global__ void __launch_bounds__(256, 1)
+decode_stream(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
+              const uint16_t *__restrict__ vc, const int *__restrict__ seqlens,
+              uint16_t *__restrict__ o, float *__restrict__ lse, float *__restrict__ ws_o,
+              float2 *__restrict__ ws_ml, long long *__restrict__ meta, int B, int Hq, int Hkv,
+              int sq, int max_len, int P, int min_piece, float scale_log2) {
+  using S = Slot<D>;
+  constexpr int CH = S::CH, RPI = S::RPI, NK = S::NK, NVG = S::NVG, KST = S::KST;
+  constexpr int MT = D / 16;
+  constexpr int TILE = kSub * D;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[kWaves * 2 * TILE];
+  // Clamped sequence lengths, staged once: segment walks then wait on LDS,
+  // never on the vector-memory counter that the K/V stream keeps busy.
+  __shared__ int lens[kMaxBatch];
 
-  const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  for (int b = threadIdx.x; b < B; b += blockDim.x) lens[b] = clamp_len(seqlens[b], max_len);
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int item = blockIdx.x * kWaves + wv;  // = piece * Hkv + kv head
+  const int g = item % Hkv, wp = item / Hkv;
+  const long long T = total_keys(lens, B);
+  // The combine step reads the total and every sequence's flattened start
+  // from here instead of re-scanning the lengths.
+  if (meta != nullptr && item == 0 && lane == 0) meta[0] = T;
+  if (T == 0) return;
+  const int P_eff = pieces_for(T, P, min_piece);
+  if (wp >= P_eff) return;
+  const long long r0 = piece_begin(wp, T, P_eff), r1 = piece_begin(wp + 1, T, P_eff);
+
   const int G = Hq / Hkv, ncol = G * sq;
-  int L = seqlens[b];
-  L = L < 0 ? 0 : (L > max_len ? max_len : L);
-  const int lo = s * chunk;
-  const int hi = min(lo + chunk, L);
-
-  // Packed query column of this lane: n = t * G + hh ([FA4-edges] §Edge 2 · GQA:
-  // row -> (seq_pos = row / G, q_head = row % G)).
   const int n = lane & 15, gq = lane >> 4;
   const bool col_ok = n < ncol;
   const int tn = col_ok ? n / G : 0;
   const int head = g * G + (col_ok ? n % G : 0);
-
-  if (lo >= hi) {
-    // Empty split. With a single split this is an empty sequence: O = 0 and
-    // LSE = -inf. With several, the combine step skips splits past the end.
-    if (n_split == 1) {
-      for (int idx = threadIdx.x; idx < ncol * D; idx += blockDim.x) {
-        const int c = idx / D, e = idx % D;
-        o[((size_t)(b * sq + c / G) * Hq + g * G + c % G) * D + e] = 0;
-      }
-      if (lse != nullptr && threadIdx.x < ncol)
-        lse[((size_t)b * Hq + g * G + threadIdx.x % G) * sq + threadIdx.x / G] = kNegInf;
-    }
-    return;
-  }
-
-  // Keys visible to this column: j < bound (tail of the split, and the
-  // bottom-right causal limit j <= L - sq + t among the new tokens).
-  const int bound = min(hi, L - sq + tn + 1);
-
-  uint16_t *klds = reinterpret_cast<uint16_t *>(smem) + w * 2 * DecodeSmem<D>::kTile;
-  uint16_t *vlds = klds + DecodeSmem<D>::kTile;
-
-  // Q^T B operand, resident for the whole split: slot k of lane group gq at
-  // k-step kk covers chunk 4 * kk + gq of the query row.
-  uint4 qop[KST];
-  {
-    const uint16_t *qrow = q + ((size_t)(b * sq + tn) * Hq + head) * D;
-#pragma unroll
-    for (int kk = 0; kk < KST; ++kk)
-      qop[kk] = col_ok ? ldg16(qrow + (4 * kk + gq) * 8) : make_uint4(0, 0, 0, 0);
-  }
-
   const size_t rstride = (size_t)Hkv * D;
-  const uint16_t *kbase = kc + ((size_t)b * max_len * Hkv + g) * D;
-  const uint16_t *vbase = vc + ((size_t)b * max_len * Hkv + g) * D;
+  const int slots = P + B;  // partial slots per KV head
+  uint16_t *klds = smem + wv * 2 * TILE;
+  uint16_t *vlds = klds + TILE;
 
-  uint4 kreg[NK];
-  uint4 vreg[NVG][4];
-  auto load_sub = [&](int j0) {
-    // Rows past `hi` are never read (they may lie past the allocation or hold
-    // garbage); zero-filled V rows keep 0 * garbage out of the P*V product.
+  // Load one sub-block (sequence b, keys [j0, j0 + 32), valid below hi) into a
+  // ring slot. Rows at or past hi are clamped to hi - 1: every load is issued
+  // unconditionally (a fixed count per sub-block keeps the wait counters exact)
+  // and reads finite data of this sequence, which the mask then excludes.
+  auto load_slot = [&](S &sl, int b, int j0, int hi) {
+    const uint16_t *kb = kc + ((size_t)b * max_len * Hkv + g) * D;
+    const uint16_t *vb = vc + ((size_t)b * max_len * Hkv + g) * D;
 #pragma unroll
     for (int qi = 0; qi < NK; ++qi) {
-      const int p = j0 + RPI * qi + lane / CH;
-      kreg[qi] = p < hi ? ldg16(kbase + (size_t)p * rstride + (lane % CH) * 8) : make_uint4(0, 0, 0, 0);
+      const int p = min(j0 + RPI * qi + lane / CH, hi - 1);
+      sl.k[qi] = ld_stream(kb + (size_t)p * rstride + (lane % CH) * 8);
     }
 #pragma unroll
     for (int hg = 0; hg < NVG; ++hg) {
       const int g4 = lane / CH + (64 / CH) * hg;
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq) {
-        const int p = j0 + 4 * g4 + qq;
-        vreg[hg][qq] = p < hi ? ldg16(vbase + (size_t)p * rstride + (lane % CH) * 8) : make_uint4(0, 0, 0, 0);
+        const int p = min(j0 + 4 * g4 + qq, hi - 1);
+        sl.v[hg][qq] = ld_stream(vb + (size_t)p * rstride + (lane % CH) * 8);
       }
     }
+    // Q^T B operand of this sequence: slot k of lane group gq at k-step kk
+    // covers chunk 4 * kk + gq of the query row (pad columns read column 0
+    // and are never written out).
+    const uint16_t *qrow = q + ((size_t)(b * sq + tn) * Hq + head) * D;
+#pragma unroll
+    for (int kk = 0; kk < KST; ++kk) sl.q[kk] = ldg16(qrow + (4 * kk + gq) * 8);
   };
 
   float m_run = kNegInf, l_run = 0.f;
@@ -154,35 +240,27 @@ decode_split_kv(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) oacc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  int j0 = lo + kSub * w;
-  if (j0 < hi) load_sub(j0);
-  for (; j0 < hi; j0 += kSub * kWaves) {
+  auto compute_slot = [&](const S &sl, const Seg &cs, int j0, bool live) {
     // K registers -> LDS (row-major, swizzled chunks).
 #pragma unroll
     for (int qi = 0; qi < NK; ++qi) {
       const int r = RPI * qi + lane / CH, c = lane % CH;
-      sts16(klds + r * D + ((c ^ k_swz<D>(r)) * 8), kreg[qi]);
+      sts16(klds + r * D + ((c ^ k_swz<D>(r)) * 8), sl.k[qi]);
     }
-    // V registers -> LDS transposed: V^T[dd][key], keys of a lane's 4-row group
-    // stay contiguous (8 bytes).
+    // V registers -> LDS transposed (V^T[dd][key]).
 #pragma unroll
     for (int hg = 0; hg < NVG; ++hg) {
       const int g4 = lane / CH + (64 / CH) * hg, c = lane % CH;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int dd = 8 * c + e;
-        const uint32_t x = col_pair(dword_of(vreg[hg][0], e >> 1), dword_of(vreg[hg][1], e >> 1), e & 1);
-        const uint32_t y = col_pair(dword_of(vreg[hg][2], e >> 1), dword_of(vreg[hg][3], e >> 1), e & 1);
+        const uint32_t x = col_pair(dword_of(sl.v[hg][0], e >> 1), dword_of(sl.v[hg][1], e >> 1), e & 1);
+        const uint32_t y = col_pair(dword_of(sl.v[hg][2], e >> 1), dword_of(sl.v[hg][3], e >> 1), e & 1);
         sts8(vlds + dd * kSub + (((g4 >> 1) ^ vt_swz(dd)) * 8) + (g4 & 1) * 4, x, y);
       }
     }
     wave_lds_sync();
 
-    // Issue the next sub-block's loads before this one's math.
-    const int jn = j0 + kSub * kWaves;
-    if (jn < hi) load_sub(jn);
-
-    // S^T tiles: rows = keys (permuted as described above), columns = queries.
     f32x4 sacc[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -192,13 +270,14 @@ decode_split_kv(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
 #pragma unroll
       for (int kk = 0; kk < KST; ++kk) {
         const int c = 4 * kk + gq;
-        sacc[t] = mfma_16x16x32(lds16(klds + r * D + ((c ^ k_swz<D>(r)) * 8)), qop[kk], sacc[t]);
+        sacc[t] = mfma_16x16x32(lds16(klds + r * D + ((c ^ k_swz<D>(r)) * 8)), sl.q[kk], sacc[t]);
       }
     }
 
-    // Online softmax in base 2 ([FA4-edges] §The correction; the 1/sqrt(d) and
-    // log2(e) factors are folded into scale_log2 and applied to fp32 scores).
-    // Masked keys are set to -inf before the max ([FA4-edges] §Edge 1).
+    // Keys visible to this column: below the segment end and, among the sq
+    // new tokens, the bottom-right causal limit j <= L - sq + t
+    // ([FA4-edges] §Edge 1: masked to -inf before the max).
+    const int bound = live ? min(cs.hi, cs.L - sq + tn + 1) : 0;
     float sv[8];
     float mloc = kNegInf;
 #pragma unroll
@@ -206,12 +285,13 @@ decode_split_kv(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int pos = j0 + 8 * gq + 4 * t + r;
-        const float x = pos < bound ? sacc[t][r] * scale_log2 : kNegInf;
-        sv[4 * t + r] = x;
-        mloc = fmaxf(mloc, x);
+        const float xs = pos < bound ? sacc[t][r] * scale_log2 : kNegInf;
+        sv[4 * t + r] = xs;
+        mloc = fmaxf(mloc, xs);
       }
     mloc = wave_xor_max(mloc, 16);
     mloc = wave_xor_max(mloc, 32);
+    // Online softmax in base 2 ([FA4-edges] §The correction).
     const float m_new = fmaxf(m_run, mloc);
     const float m_use = m_new == kNegInf ? 0.f : m_new;
     const float alpha = exp2_hw(m_run - m_use);
@@ -221,13 +301,12 @@ decode_split_kv(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
       p[i] = exp2_hw(sv[i] - m_use);
       psum += p[i];
     }
-    l_run = l_run * alpha + psum;  // per-lane partial denominator
+    l_run = l_run * alpha + psum;
     m_run = m_new;
     // Rescale O before accumulating into it ([FA4-edges] §The value MMA waits
-    // on three gates: P*V must not accumulate into an O in the old scale).
+    // on three gates).
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) oacc[mt] *= alpha;
-
     const uint4 pop = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
                                  pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7]));
 #pragma unroll
@@ -236,141 +315,237 @@ decode_split_kv(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
       oacc[mt] = mfma_16x16x32(lds16(vlds + dd * kSub + ((gq ^ vt_swz(dd)) * 8)), pop, oacc[mt]);
     }
     wave_lds_sync();
-  }
+  };
 
-  // Column denominators: the four lanes of a column hold partial sums.
-  float l_col = wave_xor_sum(l_run, 16);
-  l_col = wave_xor_sum(l_col, 32);
-
-  // Merge the four waves through LDS.
-  __syncthreads();
-  float *mo = reinterpret_cast<float *>(smem);  // [wave][col][D]
-  float *mm = mo + kWaves * kCols * D;          // [wave][col]
-  float *ml = mm + kWaves * kCols;              // [wave][col]
+  // End of a sequence segment. If the segment is the whole sequence, no other
+  // piece touches it: write the final O and LSE. Otherwise write this wave's
+  // partial for sequence b to slot wp + b of KV head g. Then reset the state.
+  auto finalize = [&](const Seg &sg) {
+    float l_col = wave_xor_sum(l_run, 16);
+    l_col = wave_xor_sum(l_col, 32);
+    const int b = sg.b;
+    if (meta != nullptr && sg.lo == 0 && g == 0 && lane == 0) meta[1 + b] = sg.start;
+    if (sg.lo == 0 && sg.hi == sg.L) {
+      if (col_ok) {
+        const float inv = l_col > 0.f ? 1.f / l_col : 0.f;
+        uint16_t *dst = o + ((size_t)(b * sq + tn) * Hq + head) * D;
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-    *reinterpret_cast<f32x4 *>(mo + (w * kCols + n) * D + 16 * mt + 4 * gq) = oacc[mt];
-  if (gq == 0) {
-    mm[w * kCols + n] = m_run;
-    ml[w * kCols + n] = l_col;
-  }
-  __syncthreads();
-
-  constexpr int SEG = D / 16;  // output elements per thread (16 threads per column)
-  const int cn = threadIdx.x >> 4, seg = (threadIdx.x & 15) * SEG;
-  if (cn >= ncol) return;
-  float M = kNegInf;
+        for (int mt = 0; mt < MT; ++mt)
+          *reinterpret_cast<uint2 *>(dst + 16 * mt + 4 * gq) =
+              make_uint2(pack_bf16x2(oacc[mt][0] * inv, oacc[mt][1] * inv),
+                         pack_bf16x2(oacc[mt][2] * inv, oacc[mt][3] * inv));
+        if (lse != nullptr && gq == 0)
+          lse[((size_t)b * Hq + head) * sq + tn] = l_col > 0.f ? kLn2 * (m_run + __log2f(l_col)) : kNegInf;
+      }
+    } else if (col_ok) {
+      const size_t slot = (size_t)g * slots + wp + b;
+      float *dst = ws_o + (slot * kCols + n) * D;
 #pragma unroll
-  for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, mm[ww * kCols + cn]);
-  float acc[SEG];
-#pragma unroll
-  for (int e = 0; e < SEG; ++e) acc[e] = 0.f;
-  float lsum = 0.f;
-  if (M != kNegInf) {
-#pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) {
-      const float sc = exp2_hw(mm[ww * kCols + cn] - M);
-      lsum += sc * ml[ww * kCols + cn];
-      const float *src = mo + (ww * kCols + cn) * D + seg;
-#pragma unroll
-      for (int e = 0; e < SEG; ++e) acc[e] += sc * src[e];
+      for (int mt = 0; mt < MT; ++mt) *reinterpret_cast<f32x4 *>(dst + 16 * mt + 4 * gq) = oacc[mt];
+      if (gq == 0) ws_ml[slot * kCols + n] = make_float2(m_run, l_col);
     }
+    m_run = kNegInf;
+    l_run = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) oacc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+
+  const Seg first = find_segment(lens, B, r0, r1);
+  if (first.b >= B) return;
+
+  // Sub-blocks of this piece, segment by segment.
+  int n_sub = 0;
+  {
+    Seg s = first;
+    do {
+      n_sub += (s.hi - s.lo + kSub - 1) / kSub;
+    } while (next_segment(s, lens, B, r1));
   }
-  const int ct = cn / G, chead = g * G + cn % G;
-  if (n_split == 1) {
-    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-    uint16_t *dst = o + ((size_t)(b * sq + ct) * Hq + chead) * D + seg;
-#pragma unroll
-    for (int e = 0; e < SEG; e += 2) {
-      *reinterpret_cast<uint32_t *>(dst + e) = pack_bf16x2(acc[e] * inv, acc[e + 1] * inv);
+
+  // Two ring slots, both explicit: the loads of sub-block i+2 go into slot A
+  // right after sub-block i (slot A) is consumed, while sub-block i+1 (slot B)
+  // is already in flight. Past the last sub-block the load iterator keeps
+  // re-reading the last valid rows and an odd count is padded with one fully
+  // masked sub-block, so the loop body has no data-dependent control flow
+  // around the slots.
+  Seg ls = first;
+  int lj = ls.lo;
+  auto advance_load = [&]() {
+    lj += kSub;
+    if (lj >= ls.hi) {
+      Seg nx = ls;
+      if (next_segment(nx, lens, B, r1)) {
+        ls = nx;
+        lj = ls.lo;
+      }
     }
-    if (lse != nullptr && (threadIdx.x & 15) == 0)
-      lse[((size_t)b * Hq + chead) * sq + ct] = lsum > 0.f ? kLn2 * (M + __log2f(lsum)) : kNegInf;
-  } else {
-    const size_t row = ((size_t)b * Hq + chead) * sq + ct;
-    float *dst = ws_o + (row * n_split + s) * D + seg;
-#pragma unroll
-    for (int e = 0; e < SEG; e += 4)
-      *reinterpret_cast<float4 *>(dst + e) = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
-    if ((threadIdx.x & 15) == 0) ws_ml[row * n_split + s] = make_float2(M, lsum);
+  };
+  Seg cs = first;
+  int cj = cs.lo;
+  auto advance_compute = [&]() {
+    cj += kSub;
+    if (cj >= cs.hi) {
+      finalize(cs);
+      if (next_segment(cs, lens, B, r1)) cj = cs.lo;
+    }
+  };
+
+  S ra, rb;
+  load_slot(ra, ls.b, lj, ls.hi);
+  advance_load();
+  load_slot(rb, ls.b, lj, ls.hi);
+  advance_load();
+  for (int i = 0; i < n_sub; i += 2) {
+    compute_slot(ra, cs, cj, true);
+    load_slot(ra, ls.b, lj, ls.hi);
+    advance_load();
+    advance_compute();
+    const bool live_b = i + 1 < n_sub;
+    compute_slot(rb, cs, cj, live_b);
+    load_slot(rb, ls.b, lj, ls.hi);
+    advance_load();
+    if (live_b) advance_compute();
   }
 }
 
 // Split-KV combine ([GQA-SM100] §Combining the KV splits, §Removing the max
-// reset): per query row, the common maximum is the max of the staged split
-// maxima; every split is rescaled by 2^(m_s - M) and the weighted fp32 sum is
-// normalised, in a fixed split order. Splits that lie past the sequence end are
-// never read (they were not written by this call) and splits with m_s = -inf
-// are skipped; an empty row gives O = 0, LSE = -inf. O is overwritten.
+// reset): per query row, the common maximum is the max of the staged piece
+// maxima, every piece is rescaled by 2^(m_s - M), and the weighted fp32 sum is
+// normalised. Only the pieces that overlap the sequence are read (all written
+// by this call); pieces whose column was fully masked (m_s = -inf) contribute
+// nothing; an empty row gives O = 0 and LSE = -inf; O is overwritten. A
+// sequence inside a single piece was finalised by the split kernel and is left
+// alone. One work-group per (sequence, KV head); the 16 threads of a column
+// each own D/16 outputs, and when the group has fewer than 16 columns the
+// idle threads form extra groups that merge disjoint, fixed subsets of the
+// pieces (w = w0 + grp, w0 + grp + NG, ...), folded together at the end in
+// group order: the result does not depend on timing.
 template <int D>
 __global__ void __launch_bounds__(256)
-combine_splits(const float *__restrict__ ws_o, const float2 *__restrict__ ws_ml,
-               const int *__restrict__ seqlens, uint16_t *__restrict__ o, float *__restrict__ lse,
-               int n_rows, int Hq, int sq, int max_len, int chunk, int n_split) {
-  constexpr int TPR = D / 4;
-  constexpr int RPB = 256 / TPR;
-  const int row = blockIdx.x * RPB + threadIdx.x / TPR;
-  if (row >= n_rows) return;
-  const int tr = threadIdx.x % TPR;
-  const int b = row / (Hq * sq), rem = row % (Hq * sq), h = rem / sq, t = rem % sq;
-  int L = seqlens[b];
-  L = L < 0 ? 0 : (L > max_len ? max_len : L);
-  const int nv = min(n_split, (L + chunk - 1) / chunk);
-  const float2 *ml = ws_ml + (size_t)row * n_split;
-  float M = kNegInf;
-  for (int sp = 0; sp < nv; ++sp) M = fmaxf(M, ml[sp].x);
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  float lsum = 0.f;
-  if (M != kNegInf) {
-    for (int sp = 0; sp < nv; ++sp) {
-      const float2 v = ml[sp];
-      if (v.x == kNegInf) continue;
-      const float sc = exp2_hw(v.x - M);
-      lsum += sc * v.y;
-      const float4 x = *reinterpret_cast<const float4 *>(ws_o + ((size_t)row * n_split + sp) * D + 4 * tr);
-      acc.x += sc * x.x;
-      acc.y += sc * x.y;
-      acc.z += sc * x.z;
-      acc.w += sc * x.w;
+combine_pieces(const float *__restrict__ ws_o, const float2 *__restrict__ ws_ml,
+               const long long *__restrict__ meta, const int *__restrict__ seqlens,
+               uint16_t *__restrict__ o, float *__restrict__ lse, int B, int Hq, int Hkv, int sq,
+               int max_len, int P, int min_piece) {
+  constexpr int SEG = D / 16;
+  __shared__ float s_m[kCols], s_l[kCols];
+  __shared__ __attribute__((aligned(16))) float s_acc[kCols][D];
+  __shared__ float s_gm[kCols], s_gl[kCols];
+  const int b = blockIdx.x, g = blockIdx.y;
+  const int tid = threadIdx.x, seg = (tid & 15) * SEG, rest = tid >> 4;
+  const int G = Hq / Hkv, ncol = G * sq;
+  const int NG = kCols / ncol;  // piece groups (>= 1)
+  const int col = rest % ncol, grp = rest / ncol;
+  const int L = clamp_len(seqlens[b], max_len);
+  int w0 = 0, w1 = -1;
+  if (L > 0) {
+    if (P <= 1) return;  // every sequence was finished by the split kernel
+    const long long T = meta[0], st = meta[1 + b];
+    const int P_eff = pieces_for(T, P, min_piece);
+    w0 = piece_of(st, T, P_eff);
+    w1 = piece_of(st + L - 1, T, P_eff);
+    if (w0 == w1) return;
+  }
+  const size_t base = (size_t)g * (P + B) + b;  // slot of piece w is base + w
+  float M = kNegInf, lsum = 0.f;
+  float acc[SEG];
+#pragma unroll
+  for (int e = 0; e < SEG; ++e) acc[e] = 0.f;
+  if (grp < NG) {
+#pragma unroll 4
+    for (int w = w0 + grp; w <= w1; w += NG) {
+      const float2 ml = ws_ml[(base + w) * kCols + col];
+      const float *src = ws_o + ((base + w) * kCols + col) * D + seg;
+      float x[SEG];
+#pragma unroll
+      for (int e = 0; e < SEG; e += 4) {
+        const float4 v = *reinterpret_cast<const float4 *>(src + e);
+        x[e] = v.x;
+        x[e + 1] = v.y;
+        x[e + 2] = v.z;
+        x[e + 3] = v.w;
+      }
+      // A piece whose column was fully masked (m = -inf, l = 0, O = 0)
+      // leaves the running state unchanged.
+      const bool live = ml.x != kNegInf;
+      const float Mn = live ? fmaxf(M, ml.x) : M;
+      const float a = live ? exp2_hw(M - Mn) : 1.f;
+      const float c = live ? exp2_hw(ml.x - Mn) : 0.f;
+      lsum = lsum * a + ml.y * c;
+#pragma unroll
+      for (int e = 0; e < SEG; ++e) acc[e] = acc[e] * a + x[e] * c;
+      M = Mn;
     }
   }
+  // Fold the piece groups into group 0, in group order.
+  if (NG > 1) {
+    for (int k = 1; k < NG; ++k) {
+      __syncthreads();
+      if (grp == k) {
+        if ((tid & 15) == 0) {
+          s_gm[col] = M;
+          s_gl[col] = lsum;
+        }
+#pragma unroll
+        for (int e = 0; e < SEG; ++e) s_acc[col][seg + e] = acc[e];
+      }
+      __syncthreads();
+      if (grp == 0) {
+        const float m2 = s_gm[col];
+        if (m2 != kNegInf) {
+          const float Mn = fmaxf(M, m2);
+          const float a = exp2_hw(M - Mn), c = exp2_hw(m2 - Mn);
+          lsum = lsum * a + s_gl[col] * c;
+#pragma unroll
+          for (int e = 0; e < SEG; ++e) acc[e] = acc[e] * a + s_acc[col][seg + e] * c;
+          M = Mn;
+        }
+      }
+    }
+  }
+  if (grp != 0) return;
+  const int ct = col / G, chead = g * G + col % G;
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-  uint16_t *dst = o + ((size_t)(b * sq + t) * Hq + h) * D + 4 * tr;
-  *reinterpret_cast<uint2 *>(dst) = make_uint2(pack_bf16x2(acc.x * inv, acc.y * inv),
-                                               pack_bf16x2(acc.z * inv, acc.w * inv));
-  if (lse != nullptr && tr == 0)
-    lse[((size_t)b * Hq + h) * sq + t] = lsum > 0.f ? kLn2 * (M + __log2f(lsum)) : kNegInf;
+  uint16_t *dst = o + ((size_t)(b * sq + ct) * Hq + chead) * D + seg;
+#pragma unroll
+  for (int e = 0; e < SEG; e += 2)
+    *reinterpret_cast<uint32_t *>(dst + e) = pack_bf16x2(acc[e] * inv, acc[e + 1] * inv);
+  if (lse != nullptr && (tid & 15) == 0)
+    lse[((size_t)b * Hq + chead) * sq + ct] = lsum > 0.f ? kLn2 * (M + __log2f(lsum)) : kNegInf;
+  (void)s_m;
+  (void)s_l;
 }
 
 }  // namespace
 
-// Host-side launchers (called by the C ABI after validation).
+// Host-side launcher (called by the C ABI after validation). Work-groups:
+// ceil(Hkv * P / 4) for the split kernel (extra waves exit at once when the
+// keys allow fewer pieces), B x Hkv for the combine.
 hipError_t launch_decode(const void *q, const void *k, const void *v, const int32_t *seqlens,
-                         void *o, float *lse, float *ws_o, float2 *ws_ml, int batch, int Hq,
-                         int Hkv, int d, int sq, int max_len, int chunk, int n_split,
+                         void *o, float *lse, float *ws_o, float2 *ws_ml, long long *meta,
+                         int batch, int Hq,
+                         int Hkv, int d, int sq, int max_len, int pieces, int min_piece,
                          float scale_log2, hipStream_t stream) {
-  const dim3 grid(n_split, Hkv, batch), block(256);
+  const dim3 block(256);
+  const dim3 grid((unsigned)(((long)Hkv * pieces + kWaves - 1) / kWaves));
   const auto *qq = static_cast<const uint16_t *>(q);
   const auto *kk = static_cast<const uint16_t *>(k);
   const auto *vv = static_cast<const uint16_t *>(v);
   auto *oo = static_cast<uint16_t *>(o);
   if (d == 128)
-    hipLaunchKernelGGL(decode_split_kv<128>, grid, block, 0, stream, qq, kk, vv, seqlens, oo, lse,
-                       ws_o, ws_ml, Hq, Hkv, sq, max_len, chunk, n_split, scale_log2);
+    hipLaunchKernelGGL((decode_stream<128>), grid, block, 0, stream, qq, kk, vv, seqlens, oo, lse,
+                       ws_o, ws_ml, meta, batch, Hq, Hkv, sq, max_len, pieces, min_piece, scale_log2);
   else
-    hipLaunchKernelGGL(decode_split_kv<64>, grid, block, 0, stream, qq, kk, vv, seqlens, oo, lse,
-                       ws_o, ws_ml, Hq, Hkv, sq, max_len, chunk, n_split, scale_log2);
+    hipLaunchKernelGGL((decode_stream<64>), grid, block, 0, stream, qq, kk, vv, seqlens, oo, lse,
+                       ws_o, ws_ml, meta, batch, Hq, Hkv, sq, max_len, pieces, min_piece, scale_log2);
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess || n_split == 1) return err;
-  const int n_rows = batch * Hq * sq;
-  const int rpb = 256 / (d / 4);
-  const dim3 cgrid((n_rows + rpb - 1) / rpb);
+  if (err != hipSuccess) return err;
+  const dim3 cgrid(batch, Hkv);
   if (d == 128)
-    hipLaunchKernelGGL(combine_splits<128>, cgrid, block, 0, stream, ws_o, ws_ml, seqlens, oo, lse,
-                       n_rows, Hq, sq, max_len, chunk, n_split);
+    hipLaunchKernelGGL(combine_pieces<128>, cgrid, block, 0, stream, ws_o, ws_ml, meta, seqlens, oo,
+                       lse, batch, Hq, Hkv, sq, max_len, pieces, min_piece);
   else
-    hipLaunchKernelGGL(combine_splits<64>, cgrid, block, 0, stream, ws_o, ws_ml, seqlens, oo, lse,
-                       n_rows, Hq, sq, max_len, chunk, n_split);
+    hipLaunchKernelGGL(combine_pieces<64>, cgrid, block, 0, stream, ws_o, ws_ml, meta, seqlens, oo,
+                       lse, batch, Hq, Hkv, sq, max_len, pieces, min_piece);
   return hipGetLastError();
 }
 

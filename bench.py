@@ -96,7 +96,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--num-splits", type=int, default=0, help="decode split override (0 = automatic)")
+    ap.add_argument("--num-splits", type=int, default=0, help="decode pieces per KV head (0 = automatic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     args = ap.parse_args()
@@ -137,11 +137,11 @@ def main():
     # K/V left in the 256 MB Infinity Cache by the previous one
     sets.append((q0, k0, v0))
     sets.append((q0.clone(), k0.clone(), v0.clone()))
-    wsz = aa.attn_decode_workspace_size(B, Hq, sq, d, S)
+    wsz = aa.attn_decode_workspace_size(B, Hq, Hkv, sq, d, S, args.num_splits)
     ws = torch.empty(wsz, dtype=torch.uint8, device=dev)
     od = torch.empty((B, sq, Hq, d), dtype=torch.bfloat16, device=dev)
     lsed = torch.empty((B, Hq, sq), dtype=torch.float32, device=dev)
-    n_split, chunk = aa.attn_decode_plan(B, Hq, Hkv, d, sq, S, args.num_splits)
+    pieces, min_piece = aa.attn_decode_plan(B, Hq, Hkv, d, sq, S, args.num_splits)
 
     # ---- prefill workload ----
     run_prefill = not args.no_prefill
@@ -220,8 +220,7 @@ def main():
             "global_batch": B,
             "seq_len": int(S),
             "kv_tokens": int(xd.seqlens.sum()),
-            "splits": n_split,
-            "chunk": chunk,
+            "pieces_per_kv_head": pieces,
             "prefill_workload": "causal-prefill b=2 h=32 d=128 s=8192 (seed 1004)" if run_prefill else None,
             "parallelism": "single-gpu",
             "device": props.name,

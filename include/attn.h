@@ -60,37 +60,47 @@ extern "C" {
 #define ATTN_ERR_LAUNCH (-5)      /* the HIP runtime refused a launch */
 #define ATTN_ERR_DEVICE (-6)      /* no usable HIP device */
 
-/* Largest number of KV splits any decode plan uses. */
-#define ATTN_MAX_SPLITS 64
-/* Every split but the last covers a multiple of this many key positions. */
-#define ATTN_SPLIT_QUANTUM 128
+/* Largest number of key pieces per KV head a decode plan uses. */
+#define ATTN_MAX_PIECES 4096
+/* Shortest piece the device cuts (fewer pieces are used when keys are few). */
+#define ATTN_MIN_PIECE 64
+/* Most sequences one decode call accepts (their lengths are staged on chip). */
+#define ATTN_MAX_BATCH 8192
 
 /*
  * Split plan of a decode call ([GQA-SM100] §Combining the KV splits: splitting
- * the KV sequence gives a small decode batch enough work-groups; each split
+ * the KV sequence gives a small decode batch enough parallel work; each split
  * returns an unnormalised partial output, its maximum and its denominator).
  *
- * The plan depends only on host integers (never on the device contents of
- * seqlens_k): key range [0, max_seqlen_k) is cut into n_split chunks of
- * `chunk` positions (a multiple of ATTN_SPLIT_QUANTUM). num_splits = 0 asks for
- * the automatic choice; a positive value is honoured after clamping to
- * [1, min(ATTN_MAX_SPLITS, ceil(max_seqlen_k / ATTN_SPLIT_QUANTUM))].
- * Host-only; touches no device. Returns ATTN_OK or ATTN_ERR_INVALID.
+ * The split is balanced on the device, from seqlens_k, without any host read:
+ * for each KV head the keys of all sequences are laid end to end and cut into
+ * P_eff = min(pieces, ceil(total_keys / min_piece)) equal pieces, one per
+ * independent worker (a 64-lane wave). A sequence inside one piece is finished
+ * by that worker; a sequence spread over several pieces is merged by the
+ * combine step. This call reports the host side of that plan: `pieces`, the
+ * number of pieces per KV head (num_splits = 0 asks for the automatic value,
+ * ceil(W / n_kv_heads) with W = 1024 workers for d = 64 and 896 for d = 128,
+ * about one work-group of four waves per CU on a 256-CU part, as measured best
+ * for HBM streaming; a positive value is honoured up to ATTN_MAX_PIECES) and
+ * `min_piece`.
+ * Host-only; touches no device. Returns ATTN_OK or an error code.
  */
 int attn_decode_plan(int batch, int n_q_heads, int n_kv_heads, int d, int seqlen_q,
-                     int max_seqlen_k, int num_splits, int *n_split, int *chunk);
+                     int max_seqlen_k, int num_splits, int *pieces, int *min_piece);
 
 /*
- * Bytes of workspace any decode plan of this shape may need:
- *   batch * n_q_heads * seqlen_q * S * (d + 2) * 4,
- * S = min(ATTN_MAX_SPLITS, ceil(max_seqlen_k / ATTN_SPLIT_QUANTUM)). The
- * workspace holds per-split fp32 partial outputs, maxima and denominators. It
- * needs no initialisation (e.g. torch.empty): every value the combine step
- * reads is written by the same call ([GQA-SM100] §Removing the max reset).
- * Returns 0 for invalid sizes. Host-only.
+ * Bytes of workspace attn_decode_ex(..., num_splits) needs for this shape
+ * (attn_decode uses num_splits = 0):
+ *   n_kv_heads * (pieces + batch) * 16 * (d + 2) * 4 + (batch + 1) * 8,
+ * or 0 when pieces == 1. It holds per-(piece, sequence) fp32 partial outputs,
+ * maxima and denominators for the (at most) pieces + batch partials of each KV
+ * head, then the key total and each sequence's flattened start. It needs no
+ * initialisation (e.g. torch.empty): every value the combine step reads is
+ * written by the same call ([GQA-SM100] §Removing the max reset).
+ * Returns 0 for invalid arguments. Host-only.
  */
-size_t attn_decode_workspace_size(int batch, int n_q_heads, int seqlen_q, int d,
-                                  int max_seqlen_k);
+size_t attn_decode_workspace_size(int batch, int n_q_heads, int n_kv_heads, int seqlen_q, int d,
+                                  int max_seqlen_k, int num_splits);
 
 /*
  * GQA KV-cache decode with split-KV and a log-sum-exp combine.
@@ -105,22 +115,26 @@ size_t attn_decode_workspace_size(int batch, int n_q_heads, int seqlen_q, int d,
  *   lse        [batch][n_q_heads][seqlen_q] fp32 natural-log LSE, overwritten;
  *              may be NULL.
  *   The seqlen_q new tokens are causal among themselves (bottom-right mask).
- *   Requires d in {64, 128} and (n_q_heads / n_kv_heads) * seqlen_q <= 16.
+ *   Requires d in {64, 128}, (n_q_heads / n_kv_heads) * seqlen_q <= 16 and
+ *   batch <= ATTN_MAX_BATCH (else ATTN_ERR_UNSUPPORTED).
  *   workspace / workspace_bytes: caller scratch of at least
- *   attn_decode_workspace_size(...) bytes; workspace == NULL forces a single
- *   split (no combine step).
+ *   attn_decode_workspace_size(...) bytes; workspace == NULL means one piece
+ *   per KV head (each sequence is streamed whole by one wave; slow on few
+ *   long sequences, but needs no scratch).
  *
- * Device work: one split kernel over (split, kv head, batch) work-groups, then,
- * when the plan has more than one split, one combine kernel over query rows.
- * Both use only fp32 arithmetic on partials, in a fixed split order, with no
- * atomics: results are deterministic and bitwise reproducible.
+ * Device work: one split kernel (one work-group of four independent waves per
+ * CU, each wave streaming one balanced piece of one KV head), then one combine
+ * kernel over (sequence, KV head) that merges the pieces of every sequence
+ * spread over several. Both use fp32 arithmetic on partials in a fixed order
+ * with no atomics: results are deterministic and bitwise reproducible.
  */
 int attn_decode(const void *q, const void *k_cache, const void *v_cache,
                 const int32_t *seqlens_k, void *o, float *lse, int n_q_heads,
                 int n_kv_heads, int d, int seqlen_q, int batch, int max_seqlen_k,
                 void *workspace, size_t workspace_bytes, void *stream);
 
-/* attn_decode with an explicit split count (0 = automatic; see attn_decode_plan). */
+/* attn_decode with an explicit number of pieces per KV head (0 = automatic;
+ * see attn_decode_plan). */
 int attn_decode_ex(const void *q, const void *k_cache, const void *v_cache,
                    const int32_t *seqlens_k, void *o, float *lse, int n_q_heads,
                    int n_kv_heads, int d, int seqlen_q, int batch, int max_seqlen_k,

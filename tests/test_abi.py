@@ -40,49 +40,41 @@ def test_status_strings_and_version():
     assert "gfx950" in aa.version()
 
 
-def _expected_plan(B, Hq, Hkv, d, sq, S, req):
-    cap = min(aa.ATTN_MAX_SPLITS, math.ceil(S / aa.ATTN_SPLIT_QUANTUM))
-    if req > 0:
-        n = req
-    else:
-        n = math.ceil(4096 / (B * Hkv))
-        n = min(n, math.ceil(S / 256))
-    n = max(1, min(n, cap))
-    chunk = math.ceil(math.ceil(S / n) / 128) * 128
-    return math.ceil(S / chunk), chunk
+def _expected_pieces(Hkv, d, req):
+    n = req if req > 0 else math.ceil((896 if d == 128 else 1024) / Hkv)
+    return max(1, min(n, aa.ATTN_MAX_PIECES))
 
 
 @pytest.mark.parametrize("shape", [
     (1, 8, 1, 64, 1, 512), (32, 64, 8, 128, 1, 8192), (16, 32, 8, 64, 4, 4096),
     (4, 32, 8, 128, 1, 131072), (3, 4, 4, 128, 1, 1), (2, 16, 1, 64, 1, 1000),
 ])
-@pytest.mark.parametrize("req", [0, 1, 2, 7, 64, 1000])
-def test_decode_plan_covers_range_and_respects_limits(shape, req):
+@pytest.mark.parametrize("req", [0, 1, 2, 7, 64, 1000, 100000])
+def test_decode_plan_and_workspace(shape, req):
     ensure_built()
     B, Hq, Hkv, d, sq, S = shape
-    n, chunk = aa.attn_decode_plan(B, Hq, Hkv, d, sq, S, req)
-    assert (n, chunk) == _expected_plan(B, Hq, Hkv, d, sq, S, req)
-    assert 1 <= n <= aa.ATTN_MAX_SPLITS
-    assert chunk % aa.ATTN_SPLIT_QUANTUM == 0
-    assert (n - 1) * chunk < S <= n * chunk  # every split non-empty for a full-length row
-    need = B * Hq * sq * n * (d + 2) * 4
-    assert aa.attn_decode_workspace_size(B, Hq, sq, d, S) >= need
+    pieces, min_piece = aa.attn_decode_plan(B, Hq, Hkv, d, sq, S, req)
+    assert pieces == _expected_pieces(Hkv, d, req)
+    assert min_piece == aa.ATTN_MIN_PIECE
+    ws = aa.attn_decode_workspace_size(B, Hq, Hkv, sq, d, S, req)
+    assert ws == (0 if pieces == 1 else Hkv * (pieces + B) * 16 * (d + 2) * 4 + (B + 1) * 8)
 
 
 def test_auto_plans_of_the_five_workloads():
     ensure_built()
-    assert aa.attn_decode_plan(1, 8, 1, 64, 1, 512) == (2, 256)
-    assert aa.attn_decode_plan(32, 64, 8, 128, 1, 8192) == (16, 512)
-    assert aa.attn_decode_plan(16, 32, 8, 64, 4, 4096) == (16, 256)
-    assert aa.attn_decode_plan(4, 32, 8, 128, 1, 131072) == (64, 2048)
+    assert aa.attn_decode_plan(1, 8, 1, 64, 1, 512) == (1024, 64)
+    assert aa.attn_decode_plan(32, 64, 8, 128, 1, 8192) == (112, 64)
+    assert aa.attn_decode_plan(16, 32, 8, 64, 4, 4096) == (128, 64)
+    assert aa.attn_decode_plan(4, 32, 8, 128, 1, 131072) == (112, 64)
 
 
 def test_workspace_size_formula():
     ensure_built()
-    assert aa.attn_decode_workspace_size(4, 32, 1, 128, 131072) == 4 * 32 * 64 * 130 * 4
-    assert aa.attn_decode_workspace_size(1, 8, 1, 64, 100) == 8 * 1 * 66 * 4
-    assert aa.attn_decode_workspace_size(0, 8, 1, 64, 100) == 0
-    assert aa.attn_decode_workspace_size(1, 8, 1, 64, 0) == 0
+    assert aa.attn_decode_workspace_size(4, 32, 8, 1, 128, 131072) == 8 * (112 + 4) * 16 * 130 * 4 + 5 * 8
+    assert aa.attn_decode_workspace_size(1, 8, 1, 1, 64, 100, 1) == 0
+    assert aa.attn_decode_workspace_size(0, 8, 1, 1, 64, 100) == 0
+    assert aa.attn_decode_workspace_size(1, 8, 1, 1, 64, 0) == 0
+    assert aa.attn_decode_workspace_size(1, 8, 3, 1, 64, 10) == 0  # Hq % Hkv != 0
 
 
 @pytest.mark.parametrize("args,status", [
@@ -93,6 +85,8 @@ def test_workspace_size_formula():
     ((16, 1, 64, 1, 1, 64), aa.ATTN_OK),                 # G = 16, the widest group
     ((32, 8, 128, 0, 1, 64), aa.ATTN_ERR_INVALID),       # sq = 0
     ((32, 8, 128, 1, 0, 64), aa.ATTN_ERR_INVALID),       # batch = 0
+    ((32, 8, 128, 1, 8192, 64), aa.ATTN_OK),             # largest batch
+    ((32, 8, 128, 1, 8193, 64), aa.ATTN_ERR_UNSUPPORTED),  # lengths no longer fit on chip
     ((32, 8, 128, 1, 1, 0), aa.ATTN_ERR_INVALID),        # max_seqlen_k = 0
 ])
 def test_plan_validation(args, status):
@@ -115,5 +109,6 @@ def test_null_pointers_are_rejected_before_any_device_work():
     odd = ctypes.c_void_p(0x1002)
     assert L.attn_decode(odd, fake, fake, fake, fake, None, 8, 1, 64, 1, 1, 16, None, 0, None) == aa.ATTN_ERR_MISALIGNED
     assert L.attn_fwd(fake, fake, odd, fake, None, 1, 1, 16, 16, 8, 8, 64, None) == aa.ATTN_ERR_MISALIGNED
-    # workspace too small for a multi-split plan
+    # workspace too small for a multi-piece plan
     assert L.attn_decode_ex(fake, fake, fake, fake, fake, None, 8, 1, 64, 1, 1, 4096, fake, 16, None, 4) == aa.ATTN_ERR_WORKSPACE
+    assert L.attn_decode_ex(fake, fake, fake, fake, fake, None, 8, 1, 64, 1, 1, 4096, fake, 16, None, -1) == aa.ATTN_ERR_INVALID

@@ -33,8 +33,8 @@ def run_decode(aa, x, num_splits=0, workspace="auto", poison=True):
     lse = G.nan_f32((B, Hq, sq)) if poison else torch.empty((B, Hq, sq), dtype=torch.float32, device="cuda")
     ws = None
     if workspace == "auto":
-        nbytes = aa.attn_decode_workspace_size(B, Hq, sq, d, S)
-        ws = torch.full((nbytes // 4,), float("nan"), dtype=torch.float32, device="cuda")
+        nbytes = aa.attn_decode_workspace_size(B, Hq, Hkv, sq, d, S, num_splits)
+        ws = torch.full((max(nbytes, 16) // 4,), float("nan"), dtype=torch.float32, device="cuda")
     aa.attn_decode(q, k, v, sl, o, lse, workspace=ws, num_splits=num_splits)
     torch.cuda.synchronize()
     return G.host_f64(o), G.host_f64(lse)
@@ -55,10 +55,12 @@ def test_decode_workload_parity(aa, cfg):
     print(f"[decode parity] {cfg}: max|dO| = {err:.3e} (max|O| {scale:.3e})", flush=True)
 
 
-@pytest.mark.parametrize("num_splits", [1, 2, 3, 5, 16, 64])
-def test_split_count_invariance(aa, num_splits):
-    x = wl.make_decode(3, 16, 4, 64, 2, 2000, [2000, 777, 129], seed=51)
-    check(aa, x, f"splits={num_splits}", num_splits=num_splits)
+@pytest.mark.parametrize("num_splits", [1, 2, 3, 5, 16, 45, 64, 4096])
+def test_piece_count_invariance(aa, num_splits):
+    """Any number of pieces per KV head gives the oracle's result (pieces cross
+    sequence boundaries, sequences span several pieces, short ones fit in one)."""
+    x = wl.make_decode(5, 16, 4, 64, 2, 2000, [2000, 777, 129, 0, 1500], seed=51)
+    check(aa, x, f"pieces={num_splits}", num_splits=num_splits)
 
 
 def test_no_workspace_single_split(aa):
@@ -76,7 +78,7 @@ def test_bitwise_determinism(aa):
 @pytest.mark.parametrize("d", [64, 128])
 def test_needles_at_block_and_split_boundaries(aa, d):
     """Key j* = 8 q (score gap >> 40) must dominate: O = v[j*] for that head."""
-    L, chunk_splits = 700, 3  # chunk 256: split boundaries at 256, 512
+    L, chunk_splits = 700, 33  # 13 x 700 keys in 33 pieces: piece boundaries fall inside sequences
     needles = [0, 1, 31, 32, 63, 127, 128, 255, 256, 257, 511, 512, 699]
     B = len(needles)
     x = wl.make_decode(B, 8, 1, d, 1, 768, [L] * B, seed=57 + d)
@@ -143,7 +145,7 @@ def test_hip_graph_replay_without_memset(aa):
     sl = G.dev_i32(x.seqlens)
     o = G.nan_like_bf16((B, sq, Hq, d))
     lse = G.nan_f32((B, Hq, sq))
-    nbytes = aa.attn_decode_workspace_size(B, Hq, sq, d, x.k.shape[1])
+    nbytes = aa.attn_decode_workspace_size(B, Hq, 8, sq, d, x.k.shape[1])
     ws = torch.full((nbytes // 4,), float("nan"), dtype=torch.float32, device="cuda")
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
