@@ -56,20 +56,46 @@ __device__ __forceinline__ float wave_xor_sum(float x, int mask) {
 // the compiler from moving memory operations across the point.
 __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-__device__ __forceinline__ uint4 ldg16(const uint16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
-__device__ __forceinline__ uint4 lds16(const uint16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
-__device__ __forceinline__ void sts16(uint16_t *p, const uint4 &v) { *reinterpret_cast<uint4 *>(p) = v; }
-__device__ __forceinline__ void sts8(uint16_t *p, uint32_t x, uint32_t y) {
-  *reinterpret_cast<uint2 *>(p) = make_uint2(x, y);
+// Transposing LDS read (ds_read_b64_tr_b16). Within each group of 16 lanes,
+// lane k supplies the address of four consecutive bf16; lane i receives, as
+// element j (j = 0..3), element (i % 4) of the four values addressed by lane
+// 4j + i / 4. If lane k of a group points at row R(k / 4), columns
+// c0 + 4 (k % 4) .. +3 of a row-major tile, lane i therefore receives column
+// c0 + i of rows R(0..3): a 4 x 16 block comes back transposed, one column per
+// lane, which is the k-major operand layout the MFMAs take.
+__device__ __forceinline__ uint2 lds_tr4(const uint16_t *p) {
+  typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+  const bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (bf16x4 __attribute__((address_space(3))) *)(reinterpret_cast<uintptr_t>(p)));
+  return __builtin_bit_cast(uint2, v);
 }
 
-// Transpose helpers for four rows r0..r3 of eight bf16 (one uint4 each): the
-// two dwords holding column e of the four rows, i.e. (r0[e], r1[e]), (r2[e], r3[e]).
-__device__ __forceinline__ uint32_t col_pair(uint32_t a, uint32_t b, int odd) {
-  return odd ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+// XOR swizzle of the 16-byte chunk index of row r of a row-major bf16 tile in
+// LDS with D = 128 (16 chunks per 256-byte row) or D = 64 (8 chunks per
+// 128-byte row; two rows share a 256-byte bank window). Conflict-free for the
+// two read patterns of the prefill tiles: 16 consecutive rows at one logical
+// chunk (a 16-lane MFMA A-operand read of K) hit 16 distinct bank groups, and
+// 4 consecutive rows (4-aligned) at 4 consecutive chunks (4-aligned) - the 32
+// lanes of a transposing read of V - hit 16 distinct bank groups.
+template <int D>
+__device__ __forceinline__ int chunk_swz(int r) {
+  if constexpr (D == 128) return (4 * (r & 3)) | ((r >> 2) & 3);
+  else return (4 * ((r >> 1) & 1)) | ((r >> 2) & 3);
 }
-__device__ __forceinline__ uint32_t dword_of(const uint4 &v, int i) {
-  return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
+
+__device__ __forceinline__ uint4 ldg16(const uint16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
+__device__ __forceinline__ uint4 lds16(const uint16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
+// A 16-byte LDS operand fetched as two 8-byte reads: on gfx950 ds_read_b64
+// sustains about twice the bytes per clock of ds_read_b128. The accesses are
+// volatile only so that the compiler does not merge them back into one
+// 16-byte read.
+__device__ __forceinline__ uint4 lds16_as_2x8(const uint16_t *p) {
+  typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
+  typedef const volatile u32x2 __attribute__((address_space(3))) *lds_ptr;
+  const u32x2 a = *(lds_ptr)(reinterpret_cast<uintptr_t>(p));
+  const u32x2 b = *(lds_ptr)(reinterpret_cast<uintptr_t>(p + 4));
+  return make_uint4(a[0], a[1], b[0], b[1]);
 }
+__device__ __forceinline__ void sts16(uint16_t *p, const uint4 &v) { *reinterpret_cast<uint4 *>(p) = v; }
 
 }  // namespace attn

@@ -29,9 +29,10 @@
 // Streaming: one work-group of four independent waves per CU. Each wave keeps
 // two sub-blocks of 32 keys in flight in a two-slot register ring (nontemporal
 // 16-byte loads; K and V are read exactly once) and, per sub-block, passes K and V
-// through a private LDS tile that changes their layout: K row-major with an
-// XOR swizzle of its 16-byte chunks, V transposed (d-major) so the P*V A
-// operand is one 16-byte LDS read. There is no work-group barrier.
+// through a private LDS tile that changes their layout to the MFMA operand
+// layouts: K and V row-major with XOR-swizzled 16-byte chunks; the P*V A
+// operand, which needs keys along its k dimension, comes from two transposing
+// ds_read_b64_tr_b16 reads of V. There is no work-group barrier.
 //
 // Key order inside a sub-block: MFMA row i of score tile t (0/1) holds key
 // 8 * (i / 4) + 4 * t + (i % 4). Lane group g (= lane / 16) then receives the
@@ -59,8 +60,15 @@ __device__ __forceinline__ int k_swz(int r) {
   }
 }
 
-// Swizzle of the 8-key unit of V^T row dd in the LDS tile [D][32].
-__device__ __forceinline__ int vt_swz(int dd) { return (dd >> 2) & 3; }
+// XOR swizzle of the 16-byte chunk index of V row r in the LDS tile [32][D].
+// The P*V operand is read transposed: the 32 lanes serviced together read
+// rows {4u..4u+3} and {8+4u..8+4u+3} (or the same plus 16) at two adjacent
+// chunks; this swizzle puts those 16 pieces on distinct bank groups.
+template <int D>
+__device__ __forceinline__ int v_swz(int r) {
+  if constexpr (D == 128) return 2 * ((r & 3) | (((r >> 3) & 1) << 2));
+  else return 2 * (((r >> 1) & 1) | (((r >> 3) & 1) << 1));
+}
 
 __device__ __forceinline__ int clamp_len(int L, int max_len) {
   return L < 0 ? 0 : (L > max_len ? max_len : L);
@@ -247,16 +255,14 @@ decode_stream(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
       const int r = RPI * qi + lane / CH, c = lane % CH;
       sts16(klds + r * D + ((c ^ k_swz<D>(r)) * 8), sl.k[qi]);
     }
-    // V registers -> LDS transposed (V^T[dd][key]).
+    // V registers -> LDS (row-major, swizzled chunks).
 #pragma unroll
     for (int hg = 0; hg < NVG; ++hg) {
       const int g4 = lane / CH + (64 / CH) * hg, c = lane % CH;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int dd = 8 * c + e;
-        const uint32_t x = col_pair(dword_of(sl.v[hg][0], e >> 1), dword_of(sl.v[hg][1], e >> 1), e & 1);
-        const uint32_t y = col_pair(dword_of(sl.v[hg][2], e >> 1), dword_of(sl.v[hg][3], e >> 1), e & 1);
-        sts8(vlds + dd * kSub + (((g4 >> 1) ^ vt_swz(dd)) * 8) + (g4 & 1) * 4, x, y);
+      for (int qq = 0; qq < 4; ++qq) {
+        const int r = 4 * g4 + qq;
+        sts16(vlds + r * D + ((c ^ v_swz<D>(r)) * 8), sl.v[hg][qq]);
       }
     }
     wave_lds_sync();
@@ -309,10 +315,19 @@ decode_stream(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
     for (int mt = 0; mt < MT; ++mt) oacc[mt] *= alpha;
     const uint4 pop = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
                                  pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7]));
+    // A operand: the same eight keys 8gq .. 8gq + 7 at column 16mt + (lane % 16),
+    // as two transposed 4-key reads.
+    const int trk = lane & 15;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const int dd = 16 * mt + (lane & 15);
-      oacc[mt] = mfma_16x16x32(lds16(vlds + dd * kSub + ((gq ^ vt_swz(dd)) * 8)), pop, oacc[mt]);
+      uint2 tr[2];
+#pragma unroll
+      for (int uu = 0; uu < 2; ++uu) {
+        const int r = 8 * gq + 4 * uu + (trk >> 2);
+        const int c = 2 * mt + ((trk & 3) >> 1);
+        tr[uu] = lds_tr4(vlds + r * D + ((c ^ v_swz<D>(r)) * 8) + 4 * (trk & 1));
+      }
+      oacc[mt] = mfma_16x16x32(make_uint4(tr[0].x, tr[0].y, tr[1].x, tr[1].y), pop, oacc[mt]);
     }
     wave_lds_sync();
   };

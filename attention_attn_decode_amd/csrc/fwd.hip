@@ -9,8 +9,10 @@
 // v_mfma_f32_32x32x16_bf16, each wave owning 32 query columns; a work-group of
 // four waves owns a 128-row query tile and shares 64-key K / V^T tiles in LDS.
 // Tiles are double-buffered: the global loads of key block i+1 are issued into
-// registers before block i's math, then written to the other LDS stage, with
-// one work-group barrier per block.
+// registers before block i's math, then written to the other LDS slot, with
+// one work-group barrier per block. K and V stay row-major in LDS (16-byte
+// writes); the P*V operand, which needs keys along its k dimension, is read
+// with the transposing ds_read_b64_tr_b16.
 //
 // Causal masking ([FA4-edges] §Edge 1 · causal masking): per (query tile, key
 // block) the block is fully visible, on the diagonal (masked to -inf before the
@@ -27,6 +29,8 @@
 // swaps bits 2 and 3 of i. Lane half h (= lane / 32) then finds, in registers
 // 8k .. 8k + 7 of its accumulator, keys 16k + 8h .. 16k + 8h + 7: the eight
 // contiguous keys of its P*V B operand for that 16-key step.
+#include <type_traits>
+
 #include "attn_device.h"
 
 namespace attn {
@@ -39,29 +43,28 @@ __device__ __forceinline__ int swap_bits23(int i) {
   return (i & ~12) | ((i >> 1) & 4) | ((i << 1) & 8);
 }
 
-// K tile in LDS: row-major [64][D], XOR swizzle of 16-byte chunks so that the
-// 16 consecutive rows of an A-operand read hit 16 distinct bank groups.
-template <int D>
-__device__ __forceinline__ int kf_swz(int r) {
-  if constexpr (D == 128) return r & 15;
-  else return (r >> 1) & 7;
-}
-// V^T tile in LDS: d-major [D][64]; 16-byte unit swizzle per row.
-__device__ __forceinline__ int vf_swz(int dd) { return (dd >> 1) & 7; }
+// Row strides (bf16 elements) of the K and V tiles in LDS. Padding replaces
+// an XOR swizzle, so every read address is a per-lane base plus a constant:
+//  - K rows of 17 (d=128) or 9 (d=64) 16-byte units: the 16 consecutive rows
+//    of an MFMA A-operand read start on 16 distinct bank groups;
+//  - V rows of 20 (d=128) or 12 (d=64) units: the 4 rows x 4 chunks that the
+//    32 lanes of a transposing read touch land on 16 distinct bank groups.
+template <int D> struct KRow { static constexpr int v = D + 8; };
+template <int D> struct VRow { static constexpr int v = D == 128 ? 160 : 96; };
 
 template <int D>
 __global__ void __launch_bounds__(256, 2)
 fwd_tile(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
          const uint16_t *__restrict__ v, uint16_t *__restrict__ o, float *__restrict__ lse,
          int Sq, int Sk, int Hq, int Hkv, int causal, float scale_log2, int n_mblocks, int BH) {
-  constexpr int CH = D / 8;              // 16-byte chunks per row
-  constexpr int TILE = kBN * D;          // bf16 elements per K or V^T tile
-  constexpr int RPT = 256 / CH;          // rows one work-group-wide load covers
-  constexpr int NKL = kBN / RPT;         // K loads per thread per block
-  constexpr int VTHREADS = (kBN / 4) * CH;  // threads holding one 4-row V group
-  constexpr int KST = D / 16;            // QK k-steps
-  constexpr int MT = D / 32;             // O^T row tiles
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * TILE];
+  constexpr int CH = D / 8;        // 16-byte chunks per row
+  constexpr int KROW = KRow<D>::v, VROW = VRow<D>::v;
+  constexpr int KT = kBN * KROW, VT = kBN * VROW;  // bf16 elements per K / V tile
+  constexpr int RPT = 256 / CH;    // rows one work-group-wide load covers
+  constexpr int NKL = kBN / RPT;   // K (and V) loads per thread per block
+  constexpr int KST = D / 16;      // QK k-steps
+  constexpr int MT = D / 32;       // O^T row tiles
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (KT + VT)];
 
   const int x = blockIdx.x;
   const int mb = n_mblocks - 1 - x / BH;  // heaviest query tile first
@@ -77,8 +80,11 @@ fwd_tile(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
   int kend = causal ? min(Sk, q0 + kBM + off) : Sk;
   if (kend < 0) kend = 0;
   const int nblk = (kend + kBN - 1) / kBN;
-  const int bound = causal ? min(Sk, qrow + off + 1) : Sk;           // this column's keys: j < bound
-  const int wave_hi = causal ? min(Sk, q0 + 32 * w + 31 + off + 1) : Sk;  // max bound over the wave
+  // Keys this column may see: j < bound. Over the wave the bound ranges from
+  // wave_lo (first column) to wave_hi (last column).
+  const int bound = causal ? min(Sk, qrow + off + 1) : Sk;
+  const int wave_lo = causal ? min(Sk, q0 + 32 * w + off + 1) : Sk;
+  const int wave_hi = causal ? min(Sk, q0 + 32 * w + 31 + off + 1) : Sk;
 
   uint4 qop[KST];
   {
@@ -91,40 +97,62 @@ fwd_tile(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
   const size_t rstride = (size_t)Hkv * D;
   const uint16_t *kb = k + ((size_t)b * Sk * Hkv + gk) * D;
   const uint16_t *vb = v + ((size_t)b * Sk * Hkv + gk) * D;
-  uint4 kreg[NKL];
-  uint4 vreg[4];
-  auto load_blk = [&](int j0) {
+  uint16_t *ktile = smem;           // K tiles, 2 slots
+  uint16_t *vtile = smem + 2 * KT;  // V tiles, 2 slots
+  uint4 kreg[NKL], vreg[NKL];
+  // Per-thread row pointers of block 0; block i adds i * 64 rows. Rows past
+  // Sk (only in a ragged last block) are clamped to Sk - 1: finite data the
+  // mask excludes, so the load count per block never changes.
+  const size_t blk_stride = (size_t)kBN * rstride;
+  const int trow = tid / CH, tcol = (tid % CH) * 8;
+  auto load_kv = [&](int blk, uint4 (&kr)[NKL], uint4 (&vr)[NKL]) {
+    const size_t base = (size_t)blk * blk_stride;
+    if (blk * kBN + kBN <= Sk) {
 #pragma unroll
-    for (int qi = 0; qi < NKL; ++qi) {
-      const int p = j0 + RPT * qi + tid / CH;
-      kreg[qi] = p < Sk ? ldg16(kb + (size_t)p * rstride + (tid % CH) * 8) : make_uint4(0, 0, 0, 0);
-    }
-    if (tid < VTHREADS) {
-      const int g4 = tid / CH;
+      for (int qi = 0; qi < NKL; ++qi) {
+        const size_t o = base + (size_t)(RPT * qi + trow) * rstride + tcol;
+        kr[qi] = ldg16(kb + o);
+        vr[qi] = ldg16(vb + o);
+      }
+    } else {
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        const int p = j0 + 4 * g4 + qq;
-        vreg[qq] = p < Sk ? ldg16(vb + (size_t)p * rstride + (tid % CH) * 8) : make_uint4(0, 0, 0, 0);
+      for (int qi = 0; qi < NKL; ++qi) {
+        const int p = min(blk * kBN + RPT * qi + trow, Sk - 1);
+        const size_t o = (size_t)p * rstride + tcol;
+        kr[qi] = ldg16(kb + o);
+        vr[qi] = ldg16(vb + o);
       }
     }
   };
-  auto store_blk = [&](int st) {
-    uint16_t *kl = smem + st * 2 * TILE;
-    uint16_t *vl = kl + TILE;
+  auto store_kv = [&](int slot, const uint4 (&kr)[NKL], const uint4 (&vr)[NKL]) {
 #pragma unroll
     for (int qi = 0; qi < NKL; ++qi) {
-      const int r = RPT * qi + tid / CH, c = tid % CH;
-      sts16(kl + r * D + ((c ^ kf_swz<D>(r)) * 8), kreg[qi]);
+      sts16(ktile + slot * KT + (RPT * qi + trow) * KROW + tcol, kr[qi]);
+      sts16(vtile + slot * VT + (RPT * qi + trow) * VROW + tcol, vr[qi]);
     }
-    if (tid < VTHREADS) {
-      const int g4 = tid / CH, c = tid % CH;
+  };
+
+  // Lane-dependent parts of the LDS read addresses; the per-instruction parts
+  // (tile t, k-step, row tile, key step) are compile-time constants added to
+  // them, which the compiler folds into the instructions' offset fields.
+  // QK A operand: K row 32t + pi(n), chunk 2kk + hl.
+  const int k_lane = swap_bits23(n) * KROW + hl * 8;
+  // P*V A operand (transposing reads of V): lane l is lane k = l % 16 of
+  // 16-lane group l / 16; the group covers output rows dd = 32mt + 16((l/16)%2)
+  // + 0..15 and keys 16ks + 8hl + 4u + 0..3; lane k addresses key row
+  // (k / 4) of those, columns 32mt + 16((l/16)%2) + 4(k % 4) .. +3.
+  const int trk = lane & 15, trhalf = (lane >> 4) & 1;
+  const int v_lane = (8 * hl + (trk >> 2)) * VROW + 16 * trhalf + 4 * (trk & 3);
+
+  auto qk = [&](int slot, f32x16 (&sa)[2]) {
+    const uint16_t *kl = ktile + slot * KT + k_lane;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int dd = 8 * c + e;
-        const uint32_t xx = col_pair(dword_of(vreg[0], e >> 1), dword_of(vreg[1], e >> 1), e & 1);
-        const uint32_t yy = col_pair(dword_of(vreg[2], e >> 1), dword_of(vreg[3], e >> 1), e & 1);
-        sts8(vl + dd * kBN + (((g4 >> 1) ^ vf_swz(dd)) * 8) + (g4 & 1) * 4, xx, yy);
-      }
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sa[t][r] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < KST; ++kk)
+        sa[t] = mfma_32x32x16(lds16(kl + 32 * t * KROW + 16 * kk), qop[kk], sa[t]);
     }
   };
 
@@ -135,76 +163,92 @@ fwd_tile(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[mt][r] = 0.f;
 
-  if (nblk > 0) load_blk(0);
-  for (int blk = 0; blk < nblk; ++blk) {
-    const int st = blk & 1;
-    store_blk(st);
-    __syncthreads();
-    if (blk + 1 < nblk) load_blk((blk + 1) * kBN);
-    const int j0 = blk * kBN;
-    if (j0 >= wave_hi) continue;  // whole block in this wave's future
-    const uint16_t *kl = smem + st * 2 * TILE;
-    const uint16_t *vl = kl + TILE;
-
-    f32x16 sacc[2];
+  // Softmax of one score block (register r of tile t holds key
+  // j0 + 32t + pi(8(r/4) + 4hl + r%4) = j0 + 32t + 16(r/8) + 8hl + (r%8)),
+  // producing the bf16 P operands; returns the rescale factor of O.
+  auto softmax = [&](f32x16 (&sa)[2], int j0, uint4 (&pop)[4], auto masked) -> float {
+    // Masking ([FA4-edges] §Edge 1): keys past this column's bound get -inf
+    // before the max. Only blocks reaching past the wave's first bound (the
+    // diagonal, the end of the keys, or blocks in the wave's future) pay it.
+    if constexpr (decltype(masked)::value) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[t][r] = 0.f;
-      const int row = 32 * t + swap_bits23(n);
-#pragma unroll
-      for (int kk = 0; kk < KST; ++kk) {
-        const int c = 2 * kk + hl;
-        sacc[t] = mfma_32x32x16(lds16(kl + row * D + ((c ^ kf_swz<D>(row)) * 8)), qop[kk], sacc[t]);
-      }
+        for (int r = 0; r < 16; ++r) {
+          const int pos = j0 + 32 * t + 16 * (r >> 3) + 8 * hl + (r & 7);
+          sa[t][r] = pos < bound ? sa[t][r] : kNegInf;
+        }
     }
-
-    // Register r of tile t holds key j0 + 32t + pi(8(r/4) + 4hl + r%4)
-    //   = j0 + 32t + 16(r/8) + 8hl + (r%8).
     float mloc = kNegInf;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int pos = j0 + 32 * t + 16 * (r >> 3) + 8 * hl + (r & 7);
-        const float xs = pos < bound ? sacc[t][r] * scale_log2 : kNegInf;
-        sacc[t][r] = xs;
-        mloc = fmaxf(mloc, xs);
-      }
+      for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sa[t][r]);
     mloc = wave_xor_max(mloc, 32);
-    const float m_new = fmaxf(m_run, mloc);
+    // Base-2 online softmax on raw scores: m is kept scaled (scale > 0, so
+    // max(scale * s) = scale * max(s)); p = 2^(s * scale - m) is one fma + exp.
+    const float m_new = fmaxf(m_run, mloc * scale_log2);
     const float m_use = m_new == kNegInf ? 0.f : m_new;
-    const float alpha = exp2_hw(m_run - m_use);
     float psum = 0.f;
-    uint4 pop[4];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         float pv[8];
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          pv[s] = exp2_hw(sacc[t][8 * hh + s] - m_use);
-          psum += pv[s];
+        for (int s2 = 0; s2 < 8; ++s2) {
+          pv[s2] = exp2_hw(__builtin_fmaf(sa[t][8 * hh + s2], scale_log2, -m_use));
+          psum += pv[s2];
         }
         pop[2 * t + hh] = make_uint4(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
                                      pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7]));
       }
+    const float alpha = exp2_hw(m_run - m_use);  // exactly 1 where the max did not move
     l_run = l_run * alpha + psum;
     m_run = m_new;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) oacc[mt] *= alpha;
+    return alpha;
+  };
 
+  // P*V for one block. O^T is rescaled before any accumulation ([FA4-edges]
+  // §The value MMA waits on three gates: P*V must not add into an O that is
+  // still in the old scale).
+  auto pv = [&](int slot, const uint4 (&pop)[4], float alpha) {
+    const uint16_t *vl = vtile + slot * VT + v_lane;
+    // Rescale O only when some column's maximum moved ([FA4-edges] §The
+    // correction); O is register-resident, so the test is one wave vote.
+    if (__any(alpha != 1.f)) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) oacc[mt] *= alpha;
+    }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const int dd = 32 * mt + n;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        // 16-key step ks covers keys 16ks + 8hl .. 16ks + 8hl + 7 for this lane.
-        const int unit = 2 * ks + hl;
-        oacc[mt] = mfma_32x32x16(lds16(vl + dd * kBN + ((unit ^ vf_swz(dd)) * 8)), pop[ks], oacc[mt]);
+        // 16-key step ks: this lane's B slots hold keys 16ks + 8hl + 0..7;
+        // the A operand is the same keys at column 32mt + n, read transposed.
+        const uint2 t0 = lds_tr4(vl + 16 * ks * VROW + 32 * mt);
+        const uint2 t1 = lds_tr4(vl + (16 * ks + 4) * VROW + 32 * mt);
+        oacc[mt] = mfma_32x32x16(make_uint4(t0.x, t0.y, t1.x, t1.y), pop[ks], oacc[mt]);
       }
     }
+  };
+
+  // Block i: its K/V move from registers into LDS slot i % 2 (whose previous
+  // tile, block i - 2, every wave finished before the last barrier); then the
+  // loads of block i + 1 go out, and block i is computed. One barrier per
+  // block.
+  if (nblk > 0) load_kv(0, kreg, vreg);
+  for (int i = 0; i < nblk; ++i) {
+    store_kv(i & 1, kreg, vreg);
+    __syncthreads();
+    if (i + 1 < nblk) load_kv(i + 1, kreg, vreg);
+    if (i * kBN >= wave_hi) continue;  // whole block in this wave's future
+    f32x16 S[2];
+    qk(i & 1, S);
+    uint4 pop[4];
+    const float alpha = (i * kBN + kBN > wave_lo) ? softmax(S, i * kBN, pop, std::true_type{})
+                                                  : softmax(S, i * kBN, pop, std::false_type{});
+    pv(i & 1, pop, alpha);
   }
 
   const float l_col = wave_xor_sum(l_run, 32);
