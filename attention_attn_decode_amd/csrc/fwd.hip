@@ -37,7 +37,7 @@ namespace attn {
 namespace {
 
 constexpr int kBM = 128;  // query rows per work-group
-constexpr int kBN = 64;   // keys per block
+constexpr int kBN = 64;   // keys per block (template default; 32 measured equal)
 
 __device__ __forceinline__ int swap_bits23(int i) {
   return (i & ~12) | ((i >> 1) & 4) | ((i << 1) & 8);
@@ -52,18 +52,22 @@ __device__ __forceinline__ int swap_bits23(int i) {
 template <int D> struct KRow { static constexpr int v = D + 8; };
 template <int D> struct VRow { static constexpr int v = D == 128 ? 160 : 96; };
 
-template <int D>
-__global__ void __launch_bounds__(256, 2)
+// BN keys per block; OCC work-groups of 4 waves per CU the register budget
+// is sized for (two: 2 waves per SIMD).
+template <int D, int BN, int OCC>
+__global__ void __launch_bounds__(256, OCC)
 fwd_tile(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
          const uint16_t *__restrict__ v, uint16_t *__restrict__ o, float *__restrict__ lse,
          int Sq, int Sk, int Hq, int Hkv, int causal, float scale_log2, int n_mblocks, int BH) {
   constexpr int CH = D / 8;        // 16-byte chunks per row
   constexpr int KROW = KRow<D>::v, VROW = VRow<D>::v;
-  constexpr int KT = kBN * KROW, VT = kBN * VROW;  // bf16 elements per K / V tile
+  constexpr int KT = BN * KROW, VT = BN * VROW;  // bf16 elements per K / V tile
   constexpr int RPT = 256 / CH;    // rows one work-group-wide load covers
-  constexpr int NKL = kBN / RPT;   // K (and V) loads per thread per block
+  constexpr int NKL = BN / RPT;   // K (and V) loads per thread per block
   constexpr int KST = D / 16;      // QK k-steps
   constexpr int MT = D / 32;       // O^T row tiles
+  constexpr int NT = BN / 32;      // 32-key score tiles per block
+  constexpr int NKS = BN / 16;     // 16-key P*V steps per block
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (KT + VT)];
 
   const int x = blockIdx.x;
@@ -79,7 +83,7 @@ fwd_tile(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
 
   int kend = causal ? min(Sk, q0 + kBM + off) : Sk;
   if (kend < 0) kend = 0;
-  const int nblk = (kend + kBN - 1) / kBN;
+  const int nblk = (kend + BN - 1) / BN;
   // Keys this column may see: j < bound. Over the wave the bound ranges from
   // wave_lo (first column) to wave_hi (last column).
   const int bound = causal ? min(Sk, qrow + off + 1) : Sk;
@@ -103,11 +107,11 @@ fwd_tile(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
   // Per-thread row pointers of block 0; block i adds i * 64 rows. Rows past
   // Sk (only in a ragged last block) are clamped to Sk - 1: finite data the
   // mask excludes, so the load count per block never changes.
-  const size_t blk_stride = (size_t)kBN * rstride;
+  const size_t blk_stride = (size_t)BN * rstride;
   const int trow = tid / CH, tcol = (tid % CH) * 8;
   auto load_kv = [&](int blk, uint4 (&kr)[NKL], uint4 (&vr)[NKL]) {
     const size_t base = (size_t)blk * blk_stride;
-    if (blk * kBN + kBN <= Sk) {
+    if (blk * BN + BN <= Sk) {
 #pragma unroll
       for (int qi = 0; qi < NKL; ++qi) {
         const size_t o = base + (size_t)(RPT * qi + trow) * rstride + tcol;
@@ -117,7 +121,7 @@ fwd_tile(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     } else {
 #pragma unroll
       for (int qi = 0; qi < NKL; ++qi) {
-        const int p = min(blk * kBN + RPT * qi + trow, Sk - 1);
+        const int p = min(blk * BN + RPT * qi + trow, Sk - 1);
         const size_t o = (size_t)p * rstride + tcol;
         kr[qi] = ldg16(kb + o);
         vr[qi] = ldg16(vb + o);
@@ -144,10 +148,10 @@ fwd_tile(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
   const int trk = lane & 15, trhalf = (lane >> 4) & 1;
   const int v_lane = (8 * hl + (trk >> 2)) * VROW + 16 * trhalf + 4 * (trk & 3);
 
-  auto qk = [&](int slot, f32x16 (&sa)[2]) {
+  auto qk = [&](int slot, f32x16 (&sa)[NT]) {
     const uint16_t *kl = ktile + slot * KT + k_lane;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < NT; ++t) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) sa[t][r] = 0.f;
 #pragma unroll
@@ -166,13 +170,13 @@ fwd_tile(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
   // Softmax of one score block (register r of tile t holds key
   // j0 + 32t + pi(8(r/4) + 4hl + r%4) = j0 + 32t + 16(r/8) + 8hl + (r%8)),
   // producing the bf16 P operands; returns the rescale factor of O.
-  auto softmax = [&](f32x16 (&sa)[2], int j0, uint4 (&pop)[4], auto masked) -> float {
+  auto softmax = [&](f32x16 (&sa)[NT], int j0, uint4 (&pop)[NKS], auto masked) -> float {
     // Masking ([FA4-edges] §Edge 1): keys past this column's bound get -inf
     // before the max. Only blocks reaching past the wave's first bound (the
     // diagonal, the end of the keys, or blocks in the wave's future) pay it.
     if constexpr (decltype(masked)::value) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int pos = j0 + 32 * t + 16 * (r >> 3) + 8 * hl + (r & 7);
@@ -181,7 +185,7 @@ fwd_tile(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     }
     float mloc = kNegInf;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sa[t][r]);
     mloc = wave_xor_max(mloc, 32);
@@ -191,7 +195,7 @@ fwd_tile(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const float m_use = m_new == kNegInf ? 0.f : m_new;
     float psum = 0.f;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         float pv[8];
@@ -212,7 +216,7 @@ fwd_tile(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
   // P*V for one block. O^T is rescaled before any accumulation ([FA4-edges]
   // §The value MMA waits on three gates: P*V must not add into an O that is
   // still in the old scale).
-  auto pv = [&](int slot, const uint4 (&pop)[4], float alpha) {
+  auto pv = [&](int slot, const uint4 (&pop)[NKS], float alpha) {
     const uint16_t *vl = vtile + slot * VT + v_lane;
     // Rescale O only when some column's maximum moved ([FA4-edges] §The
     // correction); O is register-resident, so the test is one wave vote.
@@ -223,7 +227,7 @@ fwd_tile(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
+      for (int ks = 0; ks < NKS; ++ks) {
         // 16-key step ks: this lane's B slots hold keys 16ks + 8hl + 0..7;
         // the A operand is the same keys at column 32mt + n, read transposed.
         const uint2 t0 = lds_tr4(vl + 16 * ks * VROW + 32 * mt);
@@ -242,13 +246,20 @@ fwd_tile(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     store_kv(i & 1, kreg, vreg);
     __syncthreads();
     if (i + 1 < nblk) load_kv(i + 1, kreg, vreg);
-    if (i * kBN >= wave_hi) continue;  // whole block in this wave's future
-    f32x16 S[2];
+    if (i * BN >= wave_hi) continue;  // whole block in this wave's future
+    // Wave priority follows the phase: the MFMA phases run at high priority,
+    // so when both waves of a SIMD are ready the one feeding the matrix unit
+    // issues first and the other's softmax fills the gaps.
+    f32x16 S[NT];
+    __builtin_amdgcn_s_setprio(2);
     qk(i & 1, S);
-    uint4 pop[4];
-    const float alpha = (i * kBN + kBN > wave_lo) ? softmax(S, i * kBN, pop, std::true_type{})
-                                                  : softmax(S, i * kBN, pop, std::false_type{});
+    __builtin_amdgcn_s_setprio(0);
+    uint4 pop[NKS];
+    const float alpha = (i * BN + BN > wave_lo) ? softmax(S, i * BN, pop, std::true_type{})
+                                                  : softmax(S, i * BN, pop, std::false_type{});
+    __builtin_amdgcn_s_setprio(2);
     pv(i & 1, pop, alpha);
+    __builtin_amdgcn_s_setprio(0);
   }
 
   const float l_col = wave_xor_sum(l_run, 32);
@@ -281,11 +292,11 @@ hipError_t launch_fwd(const void *q, const void *k, const void *v, void *o, floa
   const auto *vv = static_cast<const uint16_t *>(v);
   auto *oo = static_cast<uint16_t *>(o);
   if (d == 128)
-    hipLaunchKernelGGL(fwd_tile<128>, grid, block, 0, stream, qq, kk, vv, oo, lse, Sq, Sk, Hq, Hkv,
-                       causal, scale_log2, n_mblocks, BH);
+    hipLaunchKernelGGL((fwd_tile<128, kBN, 2>), grid, block, 0, stream, qq, kk, vv, oo, lse, Sq, Sk, Hq,
+                       Hkv, causal, scale_log2, n_mblocks, BH);
   else
-    hipLaunchKernelGGL(fwd_tile<64>, grid, block, 0, stream, qq, kk, vv, oo, lse, Sq, Sk, Hq, Hkv,
-                       causal, scale_log2, n_mblocks, BH);
+    hipLaunchKernelGGL((fwd_tile<64, kBN, 2>), grid, block, 0, stream, qq, kk, vv, oo, lse, Sq, Sk, Hq,
+                       Hkv, causal, scale_log2, n_mblocks, BH);
   return hipGetLastError();
 }
 

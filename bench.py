@@ -13,6 +13,16 @@ FLOPs, 4 d per visible query-key pair) is reported beside it.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 Prints one JSON line.
+
+HBM traffic (roofline.traffic) comes from two rocprofv3 counter passes over
+`bench.py --counter-run` (one 1 GiB device copy for calibration, then one
+decode call and one prefill call, nothing timed):
+  rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT -o fetch -- python bench.py --counter-run
+  rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT -o write -- python bench.py --counter-run
+  python bench.py --ingest-counters OUT/fetch_counter_collection.csv OUT/write_counter_collection.csv
+The last step (no GPU) scales each counter by what it read for the copy and
+stores bytes per launch, keyed by a hash of the kernel sources, in
+profiles/hbm_traffic_counters.json; a stale hash reports traffic as null.
 """
 from __future__ import annotations
 
@@ -69,6 +79,60 @@ def measured_traffic(kernel, src_hash, units):
     return rec.get("bytes_per_launch")
 
 
+COPY_BYTES = 1 << 30
+TRAFFIC_KERNELS = {  # stored key -> (kernel-name prefixes, sources, workload)
+    "attn_decode": (("decode_stream<", "combine_pieces<"), DECODE_SOURCES,
+                    "gqa-decode b=32 hq=64 hkv=8 d=128 sq=1 kv_len~U[1024,8192] (seed 1001)"),
+    "fwd_tile": (("fwd_tile<",), FWD_SOURCES, "causal-prefill b=2 h=32 d=128 s=8192 (seed 1004)"),
+}
+
+
+def _short_name(name):
+    name = name.replace("void ", "").replace("attn::(anonymous namespace)::", "")
+    return name.split("(")[0].strip()
+
+
+def ingest_counters(fetch_csv, write_csv):
+    """Turn the FETCH_SIZE and WRITE_SIZE passes of `--counter-run` into bytes per launch."""
+    import csv
+
+    def read(path, counter):
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+        copies = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
+        if not copies:
+            raise SystemExit(f"{path}: no copy dispatch to calibrate {counter} against")
+        scale = COPY_BYTES / (max(copies) * 1024.0)   # bytes per counted KiB
+        per = {}
+        for r in rows:
+            per.setdefault(_short_name(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+        return scale, max(copies), per
+
+    fs, fcopy, fper = read(fetch_csv, "FETCH_SIZE")
+    ws, wcopy, wper = read(write_csv, "WRITE_SIZE")
+    out = {"note": "HBM bytes per launch: rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch, "
+                   "separate passes over bench.py --counter-run), each scaled by the ratio of a "
+                   "1 GiB device copy's true bytes to what the same counter read for it.",
+           "calibration": {"copy_bytes": COPY_BYTES, "fetch_size_kib": fcopy, "write_size_kib": wcopy,
+                           "fetch_scale": round(fs, 4), "write_scale": round(ws, 4)}}
+    for key, (prefixes, srcs, workload) in TRAFFIC_KERNELS.items():
+        kern, fetch, write = {}, 0.0, 0.0
+        for nm in fper:
+            if nm.startswith(prefixes):
+                f = statistics.fmean(fper[nm])
+                w = statistics.fmean(wper.get(nm, [0.0]))
+                kern[nm] = {"fetch_kib": round(f, 3), "write_kib": round(w, 3), "dispatches": len(fper[nm])}
+                fetch += f * 1024.0 * fs
+                write += w * 1024.0 * ws
+        if kern:
+            out[key] = {"source_hash": source_hash(srcs), "workload": workload, "kernels": kern,
+                        "fetch_bytes": round(fetch), "write_bytes": round(write),
+                        "bytes_per_launch": round(fetch + write)}
+    with open(COUNTERS, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps({k: v.get("bytes_per_launch") for k, v in out.items() if isinstance(v, dict)}))
+
+
 def cpu_baseline_decode(x, d):
     """Time the fp64 oracle on the decode workload (full workload, one pass)."""
     import oracle
@@ -99,7 +163,13 @@ def main():
     ap.add_argument("--num-splits", type=int, default=0, help="decode pieces per KV head (0 = automatic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--counter-run", action="store_true",
+                    help="one copy, one decode and one prefill dispatch for rocprofv3 --pmc passes")
+    ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     args = ap.parse_args()
+    if args.ingest_counters:
+        ingest_counters(*args.ingest_counters)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1).", file=sys.stderr)
@@ -155,6 +225,20 @@ def main():
     setup_s = time.perf_counter() - t0
 
     stream = torch.cuda.current_stream()
+
+    if args.counter_run:
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        q, k, v = sets[0]
+        aa.attn_decode(q, k, v, sl, od, lsed, workspace=ws, num_splits=args.num_splits, stream=stream)
+        if run_prefill:
+            aa.attn_fwd(qp, kp, vp, op, lsep, causal=True, stream=stream)
+        torch.cuda.synchronize()
+        print("counter run done", flush=True)
+        return
 
     def step(i, evs=None):
         q, k, v = sets[i % 2]
@@ -228,7 +312,7 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "attn_decode = decode_split_kv + combine_splits",
+            "kernel": "attn_decode = decode_stream + combine_pieces",
             "achieved": round(dec_gbps, 2),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
