@@ -16,15 +16,17 @@
 //
 // Splitting ([GQA-SM100] §Combining the KV splits: splits give a small batch
 // enough parallel work; each returns an unnormalised output, its maximum and
-// its denominator). Here the split is balanced on the device: for each KV head
-// the keys of all sequences are laid end to end (sequence b occupies flattened
-// positions [start_b, start_b + L_b)), and that range is cut into P_eff equal
-// pieces. Each wave is an independent worker owning one (piece, KV head) pair,
-// so ragged lengths cost nothing in balance and there are no empty work-groups.
-// A piece may cross sequence boundaries; the wave then emits one partial per
-// sequence segment it covered. The partial of piece w for sequence b goes to
-// slot w + b of its KV head: pieces are contiguous and ordered, so (w, b) ->
-// w + b is one-to-one, and P + B slots per head always suffice.
+// its denominator). Here the split is balanced on the device, in units of the
+// 32-key sub-blocks a wave processes at a time: sequence b has
+// n_b = ceil(L_b / 32) sub-blocks, the sub-blocks of all sequences are laid end
+// to end (sequence b occupies flattened units [start_b, start_b + n_b)), and
+// that range is cut into P_eff equal pieces. Each wave is an independent worker
+// owning one (piece, KV head) pair, so every wave runs the same number of
+// sub-blocks (to within one) however ragged the lengths, and there are no empty
+// work-groups. A piece may cross sequence boundaries; the wave then emits one
+// partial per sequence segment it covered. The partial of piece w for sequence
+// b goes to slot w + b of its KV head: pieces are contiguous and ordered, so
+// (w, b) -> w + b is one-to-one, and P + B slots per head always suffice.
 //
 // Streaming: one work-group of four independent waves per CU. Each wave keeps
 // two sub-blocks of 32 keys in flight in a two-slot register ring (nontemporal
@@ -80,24 +82,27 @@ __device__ __forceinline__ uint4 ld_stream(const uint16_t *p) {
   return make_uint4(t[0], t[1], t[2], t[3]);
 }
 
-// Sum over all sequences of the (clamped) lengths in `lens` (every lane gets it).
-__device__ long long total_keys(const int *lens, int B) {
+// Sub-blocks of a sequence of L keys.
+__device__ __forceinline__ int units_of(int L) { return (L + kSub - 1) / kSub; }
+
+// Sum over all sequences of their sub-block counts (every lane gets it).
+__device__ long long total_units(const int *lens, int B) {
   const int lane = threadIdx.x & 63;
   long long t = 0;
-  for (int b = lane; b < B; b += 64) t += lens[b];
+  for (int b = lane; b < B; b += 64) t += units_of(lens[b]);
   for (int m = 1; m < 64; m <<= 1) t += __shfl_xor(t, m, 64);
   return t;
 }
 
 // Number of pieces per KV head: the requested P, but no piece shorter than
-// min_piece keys (so tiny inputs do not fan out into empty work).
-__device__ __forceinline__ int pieces_for(long long T, int P, int min_piece) {
-  const long long by_len = (T + min_piece - 1) / min_piece;
+// min_units sub-blocks (so tiny inputs do not fan out into empty work).
+__device__ __forceinline__ int pieces_for(long long T, int P, int min_units) {
+  const long long by_len = (T + min_units - 1) / min_units;
   return (int)(by_len < P ? (by_len < 1 ? 1 : by_len) : P);
 }
 
-// Piece w of P_eff covers flattened keys [w*T/P_eff, (w+1)*T/P_eff); the piece
-// holding flattened key x is ((x + 1) * P_eff - 1) / T.
+// Piece w of P_eff covers flattened units [w*T/P_eff, (w+1)*T/P_eff); the
+// piece holding flattened unit x is ((x + 1) * P_eff - 1) / T.
 __device__ __forceinline__ long long piece_begin(int w, long long T, int P_eff) {
   return (long long)w * T / P_eff;
 }
@@ -107,35 +112,41 @@ __device__ __forceinline__ int piece_of(long long x, long long T, int P_eff) {
 
 struct Seg {
   int b;            // sequence
-  int lo, hi;       // local key range [lo, hi) of this segment
+  int lo, hi;       // local key range [lo, hi) of this segment (lo % 32 == 0)
   int L;            // clamped sequence length
-  long long start;  // flattened start of the sequence
+  long long start;  // flattened unit where the sequence starts
 };
 
-// The sequence containing flattened key x (x < total): wave-wide scan over the
-// clamped lengths, 64 sequences at a time.
+// Key end of a segment of sequence (start, L) cut at flattened unit r1.
+__device__ __forceinline__ int seg_hi(long long start, int L, long long r1) {
+  const long long e = (r1 - start) * kSub;
+  return (int)(e < L ? e : L);
+}
+
+// The sequence containing flattened unit x (x < total): wave-wide scan over
+// the sub-block counts, 64 sequences at a time.
 __device__ Seg find_segment(const int *lens, int B, long long x, long long r1) {
   const int lane = threadIdx.x & 63;
   long long carry = 0;
   for (int base = 0; base < B; base += 64) {
     const int b = base + lane;
     const int L = b < B ? lens[b] : 0;
-    long long incl = L;
+    const int n = units_of(L);
+    long long incl = n;
     for (int off = 1; off < 64; off <<= 1) {
       const long long y = __shfl_up(incl, off, 64);
       if (lane >= off) incl += y;
     }
-    const long long st = carry + incl - L;
-    const unsigned long long hit = __ballot(L > 0 && st <= x && x < st + L);
+    const long long st = carry + incl - n;
+    const unsigned long long hit = __ballot(n > 0 && st <= x && x < st + n);
     if (hit) {
       const int h = __ffsll((long long)hit) - 1;
       Seg s;
       s.b = base + h;
       s.start = __shfl(st, h, 64);
       s.L = __shfl(L, h, 64);
-      s.lo = (int)(x - s.start);
-      const long long e = r1 - s.start;
-      s.hi = (int)(e < s.L ? e : s.L);
+      s.lo = (int)(x - s.start) * kSub;
+      s.hi = seg_hi(s.start, s.L, r1);
       return s;
     }
     carry += __shfl(incl, 63, 64);
@@ -144,9 +155,9 @@ __device__ Seg find_segment(const int *lens, int B, long long x, long long r1) {
   return none;
 }
 
-// Next non-empty sequence segment before flattened position r1.
+// Next non-empty sequence segment before flattened unit r1.
 __device__ bool next_segment(Seg &s, const int *lens, int B, long long r1) {
-  long long st = s.start + s.L;
+  long long st = s.start + units_of(s.L);
   for (int b = s.b + 1; b < B && st < r1; ++b) {
     const int L = lens[b];
     if (L > 0) {
@@ -154,8 +165,7 @@ __device__ bool next_segment(Seg &s, const int *lens, int B, long long r1) {
       s.start = st;
       s.L = L;
       s.lo = 0;
-      const long long e = r1 - st;
-      s.hi = (int)(e < L ? e : L);
+      s.hi = seg_hi(st, L, r1);
       return true;
     }
   }
@@ -180,7 +190,7 @@ decode_stream(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
               const uint16_t *__restrict__ vc, const int *__restrict__ seqlens,
               uint16_t *__restrict__ o, float *__restrict__ lse, float *__restrict__ ws_o,
               float2 *__restrict__ ws_ml, long long *__restrict__ meta, int B, int Hq, int Hkv,
-              int sq, int max_len, int P, int min_piece, float scale_log2) {
+              int sq, int max_len, int P, int min_units, float scale_log2) {
   using S = Slot<D>;
   constexpr int CH = S::CH, RPI = S::RPI, NK = S::NK, NVG = S::NVG, KST = S::KST;
   constexpr int MT = D / 16;
@@ -195,12 +205,12 @@ decode_stream(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int item = blockIdx.x * kWaves + wv;  // = piece * Hkv + kv head
   const int g = item % Hkv, wp = item / Hkv;
-  const long long T = total_keys(lens, B);
+  const long long T = total_units(lens, B);
   // The combine step reads the total and every sequence's flattened start
   // from here instead of re-scanning the lengths.
   if (meta != nullptr && item == 0 && lane == 0) meta[0] = T;
   if (T == 0) return;
-  const int P_eff = pieces_for(T, P, min_piece);
+  const int P_eff = pieces_for(T, P, min_units);
   if (wp >= P_eff) return;
   const long long r0 = piece_begin(wp, T, P_eff), r1 = piece_begin(wp + 1, T, P_eff);
 
@@ -367,15 +377,7 @@ decode_stream(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
 
   const Seg first = find_segment(lens, B, r0, r1);
   if (first.b >= B) return;
-
-  // Sub-blocks of this piece, segment by segment.
-  int n_sub = 0;
-  {
-    Seg s = first;
-    do {
-      n_sub += (s.hi - s.lo + kSub - 1) / kSub;
-    } while (next_segment(s, lens, B, r1));
-  }
+  const int n_sub = (int)(r1 - r0);  // sub-blocks of this piece
 
   // Two ring slots, both explicit: the loads of sub-block i+2 go into slot A
   // right after sub-block i (slot A) is consumed, while sub-block i+1 (slot B)
@@ -440,7 +442,7 @@ __global__ void __launch_bounds__(256)
 combine_pieces(const float *__restrict__ ws_o, const float2 *__restrict__ ws_ml,
                const long long *__restrict__ meta, const int *__restrict__ seqlens,
                uint16_t *__restrict__ o, float *__restrict__ lse, int B, int Hq, int Hkv, int sq,
-               int max_len, int P, int min_piece) {
+               int max_len, int P, int min_units) {
   constexpr int SEG = D / 16;
   __shared__ float s_m[kCols], s_l[kCols];
   __shared__ __attribute__((aligned(16))) float s_acc[kCols][D];
@@ -455,9 +457,9 @@ combine_pieces(const float *__restrict__ ws_o, const float2 *__restrict__ ws_ml,
   if (L > 0) {
     if (P <= 1) return;  // every sequence was finished by the split kernel
     const long long T = meta[0], st = meta[1 + b];
-    const int P_eff = pieces_for(T, P, min_piece);
+    const int P_eff = pieces_for(T, P, min_units);
     w0 = piece_of(st, T, P_eff);
-    w1 = piece_of(st + L - 1, T, P_eff);
+    w1 = piece_of(st + units_of(L) - 1, T, P_eff);
     if (w0 == w1) return;
   }
   const size_t base = (size_t)g * (P + B) + b;  // slot of piece w is base + w
@@ -542,25 +544,26 @@ hipError_t launch_decode(const void *q, const void *k, const void *v, const int3
                          float scale_log2, hipStream_t stream) {
   const dim3 block(256);
   const dim3 grid((unsigned)(((long)Hkv * pieces + kWaves - 1) / kWaves));
+  const int min_units = min_piece > kSub ? min_piece / kSub : 1;
   const auto *qq = static_cast<const uint16_t *>(q);
   const auto *kk = static_cast<const uint16_t *>(k);
   const auto *vv = static_cast<const uint16_t *>(v);
   auto *oo = static_cast<uint16_t *>(o);
   if (d == 128)
     hipLaunchKernelGGL((decode_stream<128>), grid, block, 0, stream, qq, kk, vv, seqlens, oo, lse,
-                       ws_o, ws_ml, meta, batch, Hq, Hkv, sq, max_len, pieces, min_piece, scale_log2);
+                       ws_o, ws_ml, meta, batch, Hq, Hkv, sq, max_len, pieces, min_units, scale_log2);
   else
     hipLaunchKernelGGL((decode_stream<64>), grid, block, 0, stream, qq, kk, vv, seqlens, oo, lse,
-                       ws_o, ws_ml, meta, batch, Hq, Hkv, sq, max_len, pieces, min_piece, scale_log2);
+                       ws_o, ws_ml, meta, batch, Hq, Hkv, sq, max_len, pieces, min_units, scale_log2);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const dim3 cgrid(batch, Hkv);
   if (d == 128)
     hipLaunchKernelGGL(combine_pieces<128>, cgrid, block, 0, stream, ws_o, ws_ml, meta, seqlens, oo,
-                       lse, batch, Hq, Hkv, sq, max_len, pieces, min_piece);
+                       lse, batch, Hq, Hkv, sq, max_len, pieces, min_units);
   else
     hipLaunchKernelGGL(combine_pieces<64>, cgrid, block, 0, stream, ws_o, ws_ml, meta, seqlens, oo,
-                       lse, batch, Hq, Hkv, sq, max_len, pieces, min_piece);
+                       lse, batch, Hq, Hkv, sq, max_len, pieces, min_units);
   return hipGetLastError();
 }
 
