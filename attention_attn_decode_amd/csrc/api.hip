@@ -128,7 +128,7 @@ int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, i
     return ATTN_ERR_INVALID;
   if (n_q_heads % n_kv_heads != 0) return ATTN_ERR_INVALID;
   if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
-  const long wgs = (long)((seqlen_q + 127) / 128) * batch * n_q_heads;
+  const long wgs = (long)((seqlen_q + 255) / 256) * batch * n_q_heads;  // 256-row query tiles
   if (wgs > 0x7fffffffL) return ATTN_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (lse && !aligned4(lse)))
     return ATTN_ERR_MISALIGNED;

@@ -83,7 +83,7 @@ COPY_BYTES = 1 << 30
 TRAFFIC_KERNELS = {  # stored key -> (kernel-name prefixes, sources, workload)
     "attn_decode": (("decode_stream<", "combine_pieces<"), DECODE_SOURCES,
                     "gqa-decode b=32 hq=64 hkv=8 d=128 sq=1 kv_len~U[1024,8192] (seed 1001)"),
-    "fwd_tile": (("fwd_tile<",), FWD_SOURCES, "causal-prefill b=2 h=32 d=128 s=8192 (seed 1004)"),
+    "fwd_pp": (("fwd_pp<",), FWD_SOURCES, "causal-prefill b=2 h=32 d=128 s=8192 (seed 1004)"),
 }
 
 
@@ -338,7 +338,7 @@ def main():
         tf = fl / (pre_mean * 1e-3) / 1e12
         result["prefill"] = {
             "bound": "mfma",
-            "kernel": "fwd_tile",
+            "kernel": "fwd_pp",
             "ms_mean": round(pre_mean, 5),
             "ms_median": round(statistics.median(pre_ms), 5),
             "flops": fl,
@@ -346,7 +346,7 @@ def main():
             "peak": BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(tf / BF16_PEAK_TFLOPS, 4),
-            "traffic": measured_traffic("fwd_tile", source_hash(FWD_SOURCES), None),
+            "traffic": measured_traffic("fwd_pp", source_hash(FWD_SOURCES), None),
         }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline_decode(xd, d)

@@ -147,8 +147,8 @@ int attn_decode_ex(const void *q, const void *k_cache, const void *v_cache,
  * [batch][seqlen_k][n_kv_heads][d], all bf16; o like q; lse
  * [batch][n_q_heads][seqlen_q] fp32 (may be NULL). causal != 0 applies the
  * bottom-right mask (query i sees keys j <= i + seqlen_k - seqlen_q).
- * Requires d == 128 or d == 64. Work-groups of 128 query rows are launched
- * heaviest first (longest visible key range first).
+ * Requires d == 128 or d == 64. Work-groups of eight waves own 256 query rows
+ * and are launched heaviest first (longest visible key range first).
  */
 int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int causal,
              int batch, int seqlen_q, int seqlen_k, int n_q_heads, int n_kv_heads, int d,
