@@ -47,6 +47,14 @@ __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2
 __device__ __forceinline__ float wave_xor_max(float x, int mask) {
   return fmaxf(x, __shfl_xor(x, mask, 64));
 }
+// max(x[l], x[l ^ 32]) in every lane l, without LDS: v_permlane32_swap
+// exchanges the upper half of its first operand with the lower half of its
+// second, so with both operands x the two results hold, in every lane, the
+// lane's own value and its partner's.
+__device__ __forceinline__ float wave_max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 __device__ __forceinline__ float wave_xor_sum(float x, int mask) {
   return x + __shfl_xor(x, mask, 64);
 }

@@ -40,6 +40,15 @@ __device__ __forceinline__ int swap_bits23(int i) {
   return (i & ~12) | ((i >> 1) & 4) | ((i << 1) & 8);
 }
 
+// f(I), f(I + 1), ..., f(N - 1) with the index a compile-time constant.
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
 // Row strides (bf16 elements) of the K and V tiles in LDS. Padding replaces
 // an XOR swizzle, so every read address is a per-lane base plus a constant:
 //  - K rows of 17 (d=128) or 9 (d=64) 16-byte units: the 16 consecutive rows
@@ -190,7 +199,7 @@ fwd_pp(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, S[t][r]);
-    mloc = wave_xor_max(mloc, 32);
+    mloc = wave_max_halves(mloc);
     const float mblk = mloc * scale_log2;
     const float m_new = mblk > m_run + kRescaleLog2 ? mblk : m_run;
     const float m_use = m_new == kNegInf ? 0.f : m_new;
@@ -219,8 +228,62 @@ fwd_pp(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     }
   };
 
+  // Both products of a phase as one stream of 2 * NPV MFMAs: first P*V(j-1)
+  // (16-key step outer, so each P operand dies after its last use), then
+  // S(j). Every MFMA's LDS operand (a transposed V pair or a K row chunk) is
+  // read KDEP MFMAs ahead through a small register ring, so the S(j) reads
+  // already run under the last P*V MFMAs and no read waits on LDS latency.
+  constexpr int NPV = MT * NKS;  // P*V MFMAs per block (= QK MFMAs, NT * KST)
+  constexpr int KDEP = 3;
+  static_assert(NPV == NT * KST, "both products have the same MFMA count");
+  auto pv_qk = [&](int vslot, int kslot, int j) {
+    const uint16_t *vl = vtile + vslot * VT + v_lane;
+    const uint16_t *kl = ktile + kslot * KT + k_lane;
+    auto rd = [&](int g) {
+      if (g < NPV) {
+        const int ks = g / MT, mt = g % MT;
+        const uint2 t0 = lds_tr4(vl + 16 * ks * VROW + 32 * mt);
+        const uint2 t1 = lds_tr4(vl + (16 * ks + 4) * VROW + 32 * mt);
+        return make_uint4(t0.x, t0.y, t1.x, t1.y);
+      }
+      const int m = g - NPV;
+      return lds16(kl + 32 * (m % NT) * KROW + 16 * (m / NT));
+    };
+    uint4 ring[KDEP];
+#pragma unroll
+    for (int g = 0; g < KDEP; ++g) ring[g] = rd(g);
+    static_for<0, 2 * NPV>([&](auto gc) {
+      constexpr int g = decltype(gc)::value;
+      const uint4 a = ring[g % KDEP];
+      if constexpr (g + KDEP < 2 * NPV) ring[g % KDEP] = rd(g + KDEP);
+      // This group's share of the staging (see stage below), unconditional in
+      // the steady range: blocks past the last are clamped re-reads of the
+      // last rows, written to a slot nobody reads again.
+      if constexpr (g == 2) store_blk(j + 1 - G);
+      if constexpr (g == 6) load_blk(j + 2 - G);
+      if constexpr (g < NPV) {
+        constexpr int ks = g / MT, mt = g % MT;
+        oacc[mt] = mfma_32x32x16(a, pop[ks], oacc[mt]);
+      } else {
+        constexpr int m = g - NPV, t = m % NT, kk = m / NT;
+        if constexpr (kk == 0) S[t] = mfma_32x32x16(a, qop[kk], f32x16{});
+        else S[t] = mfma_32x32x16(a, qop[kk], S[t]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+  // Staging, done in the MFMA phase, whose wave mostly waits on the matrix
+  // unit: in its phase j group A writes K(j+1) (into the slot K(j-1) held,
+  // last read in the previous half-step) and loads K(j+2); group B, half a
+  // step later, writes V(j) (into V(j-2)'s slot) and loads V(j+1). Each tile
+  // is visible one barrier before its first reader.
+  auto stage = [&](int j) {
+    if (j + 1 - G < nblk) store_blk(j + 1 - G);
+    if (j + 2 - G < nblk) load_blk(j + 2 - G);
+  };
   auto mfma_phase = [&](int j) {
     __builtin_amdgcn_s_setprio(2);
+    stage(j);
     if (j >= 1 && j - 1 < nbw) pv((j - 1) & 1);
     if (j < nbw) qk(j & 1);
     __builtin_amdgcn_s_setprio(0);
@@ -230,10 +293,6 @@ fwd_pp(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
       if (j * BN + BN > wave_lo) softmax(j * BN, std::true_type{});
       else softmax(j * BN, std::false_type{});
     }
-    // Group A writes K(j+1) during its phase j, group B writes V(j+1) during
-    // its phase j (one half-step later); each then loads its next block.
-    if (j + 1 < nblk && (G == 1 || j >= 0)) store_blk(j + 1);
-    if (j + 2 < nblk && (G == 1 || j >= 0)) load_blk(j + 2);
   };
 
   // Prologue: K(0) into slot 0; group A holds K(1), group B V(0) in registers.
@@ -246,13 +305,32 @@ fwd_pp(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     if (G == 1) load_blk(0);
   }
   __syncthreads();
-  // Group B starts one phase later (its phase "-1" stages V(0)); both groups
-  // pass the same number of barriers.
-  if (G == 1) {
-    valu_phase(-1);
+  // Group B starts one phase later; both groups pass the same number of
+  // barriers.
+  if (G == 1) __syncthreads();
+  // Steps j = 0 .. nblk. The steady range 1 <= j < nbw, where the MFMA phase
+  // has both products, is a loop of its own, so its register assignment is
+  // not merged with the edge steps'.
+  int j = 0;
+  for (; j <= nblk && (j == 0 || j >= nbw); ++j) {  // j = 0, or a wave with nbw <= 1
+    mfma_phase(j);
+    __syncthreads();
+    valu_phase(j);
+    __syncthreads();
+    if (j == 0 && nbw > 1) {
+      ++j;
+      break;
+    }
+  }
+  for (; j < nbw; ++j) {
+    __builtin_amdgcn_s_setprio(2);
+    pv_qk((j - 1) & 1, j & 1, j);
+    __builtin_amdgcn_s_setprio(0);
+    __syncthreads();
+    valu_phase(j);
     __syncthreads();
   }
-  for (int j = 0; j <= nblk; ++j) {
+  for (; j <= nblk; ++j) {
     mfma_phase(j);
     __syncthreads();
     valu_phase(j);
