@@ -72,10 +72,13 @@ extern "C" {
  * the KV sequence gives a small decode batch enough parallel work; each split
  * returns an unnormalised partial output, its maximum and its denominator).
  *
- * The split is balanced on the device, from seqlens_k, without any host read:
- * for each KV head the keys of all sequences are laid end to end and cut into
- * P_eff = min(pieces, ceil(total_keys / min_piece)) equal pieces, one per
- * independent worker (a 64-lane wave). A sequence inside one piece is finished
+ * The split is balanced on the device, from seqlens_k, without any host read,
+ * in units of the 32-key sub-blocks a worker processes at a time: sequence b
+ * has ceil(L_b / 32) of them; for each KV head the sub-blocks of all
+ * sequences are laid end to end and cut into
+ * P_eff = min(pieces, ceil(total_sub_blocks / (min_piece / 32))) equal pieces,
+ * one per independent worker (a 64-lane wave), so every worker runs the same
+ * number of sub-blocks to within one. A sequence inside one piece is finished
  * by that worker; a sequence spread over several pieces is merged by the
  * combine step. This call reports the host side of that plan: `pieces`, the
  * number of pieces per KV head (num_splits = 0 asks for the automatic value,
