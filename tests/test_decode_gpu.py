@@ -185,3 +185,37 @@ def test_errors_are_reported_without_launch(aa):
     assert e.value.status == aa.ATTN_ERR_WORKSPACE
     torch.cuda.synchronize()
     assert float(o.abs().max()) == 0.0  # nothing was written
+
+
+@pytest.mark.parametrize("shape", [
+    # B, Hq, Hkv, d, sq, lengths
+    (2, 4, 2, 64, 1, [70, 33]),
+    (1, 2, 1, 64, 3, [65]),
+    (2, 3, 3, 128, 2, [1, 40]),
+])
+def test_tiny_shapes_against_brute_force(aa, shape):
+    """Tiny shapes against the pure-Python scalar oracle (math.fsum, own bf16 decode)."""
+    from oracle.brute import brute_attention
+    B, Hq, Hkv, d, sq, lens = shape
+    x = wl.make_decode(B, Hq, Hkv, d, sq, max(lens), lens, seed=91 + d + sq)
+    Ob, Lb = brute_attention(x.q, x.k, x.v, x.seqlens, True)
+    O_ref, L_ref = np.array(Ob, dtype=np.float64), np.array(Lb, dtype=np.float64)
+    for ns in (0, 1, 3):
+        o, lse = run_decode(aa, x, num_splits=ns)
+        G.assert_parity(o, lse, O_ref, L_ref, f"brute {shape} pieces={ns}")
+
+
+def test_gqa_equals_mha_with_repeated_kv_heads(aa):
+    """GQA output equals MHA over K/V heads repeated G times (head h reads KV head h // G)."""
+    B, Hq, Hkv, d, sq, S = 3, 8, 2, 128, 2, 700
+    x = wl.make_decode(B, Hq, Hkv, d, sq, S, [700, 257, 64], seed=97)
+    o_gqa, l_gqa = run_decode(aa, x)
+    G_ = Hq // Hkv
+    x.k = np.ascontiguousarray(np.repeat(x.k, G_, axis=2))
+    x.v = np.ascontiguousarray(np.repeat(x.v, G_, axis=2))
+    o_mha, l_mha = run_decode(aa, x)
+    # Different column packing changes only the fp32 summation order.
+    assert np.abs(o_gqa - o_mha).max() <= 8e-3
+    assert np.abs(l_gqa - l_mha).max() <= 1e-4 * max(1.0, np.abs(l_mha).max())
+    O_ref, L_ref = oracle.attention(x.q, x.k, x.v, x.seqlens, True)
+    G.assert_parity(o_mha, l_mha, O_ref, L_ref, "mha-repeated")

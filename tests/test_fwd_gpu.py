@@ -91,3 +91,15 @@ def test_fwd_deterministic(aa):
     a = run_fwd(aa, x)
     b = run_fwd(aa, x)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_fwd_gqa_equals_mha_with_repeated_kv_heads(aa):
+    """Prefill GQA equals MHA over K/V heads repeated G times (head h reads KV head h // G)."""
+    B, Sq, Sk, Hq, Hkv, d = 1, 300, 300, 4, 2, 128
+    x = wl.make_prefill(B, Hq, Hkv, d, Sq, Sk, seed=99)
+    o_gqa, l_gqa = run_fwd(aa, x, True)
+    x.k = np.ascontiguousarray(np.repeat(x.k, Hq // Hkv, axis=2))
+    x.v = np.ascontiguousarray(np.repeat(x.v, Hq // Hkv, axis=2))
+    o_mha, l_mha = run_fwd(aa, x, True)
+    # The same kernel computes both with identical per-column arithmetic.
+    assert np.array_equal(o_gqa, o_mha) and np.array_equal(l_gqa, l_mha)
