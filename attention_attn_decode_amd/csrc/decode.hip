@@ -557,8 +557,8 @@ hipError_t launch_decode(const void *q, const void *k, const void *v, const int3
                        ws_o, ws_ml, meta, batch, Hq, Hkv, sq, max_len, pieces, min_units, scale_log2);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  // With one piece per KV head every sequence is finished by the split kernel.
-  if (pieces <= 1) return hipSuccess;
+  // Launched even with one piece per KV head: it writes O = 0 and LSE = -inf
+  // for empty sequences, which no split-kernel wave visits.
   const dim3 cgrid(batch, Hkv);
   if (d == 128)
     hipLaunchKernelGGL(combine_pieces<128>, cgrid, block, 0, stream, ws_o, ws_ml, meta, seqlens, oo,
