@@ -16,6 +16,8 @@ Every function is parity-pinned by tests in ``tests/test_oracle_pins.py``.
 """
 from .attention import (  # noqa: F401
     bf16_bits_to_f64,
+    f16_bits_to_f64,
+    to_f64,
     attention,
     attention_rows,
     probabilities,

@@ -6,7 +6,7 @@ Definition followed ([FA4-decode] §Recap on the FA4 forward pass):
     S = Q K^T / sqrt(d),  P = softmax(S) row-wise,  O = P V.
 Tiled online-softmax kernels reach exactly this result up to rounding order
 (same section), so the oracle is the definition itself, in fp64, from the same
-bf16 bytes (bf16 -> fp64 is exact).
+bf16 or fp16 bytes (both convert to fp64 exactly).
 
 Readings where the pages leave a step open (each is listed in the design notes):
   * GQA head map: query head h reads KV head h // G with G = Hq / Hkv, i.e. the
@@ -32,6 +32,20 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     """Exact bf16 -> fp64: the bf16 pattern is the top half of a float32."""
     b = np.ascontiguousarray(bits, dtype=np.uint16)
     return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def f16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact IEEE binary16 -> fp64 (NumPy's half-precision type as the decoder)."""
+    return np.ascontiguousarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def to_f64(bits: np.ndarray, dtype: str = "bf16") -> np.ndarray:
+    """Decode 16-bit element patterns of the given type ("bf16" or "f16") to fp64."""
+    if dtype == "bf16":
+        return bf16_bits_to_f64(bits)
+    if dtype == "f16":
+        return f16_bits_to_f64(bits)
+    raise ValueError(f"unknown element type {dtype!r}")
 
 
 def _visible(L: int, sq: int, t: int, causal: bool) -> int:
@@ -67,7 +81,7 @@ def _attend(qrows: np.ndarray, kk: np.ndarray, vv: np.ndarray, nvis: np.ndarray,
     return O, lse
 
 
-def attention(q, k, v, seqlens=None, causal=True, row_block=512):
+def attention(q, k, v, seqlens=None, causal=True, row_block=512, dtype="bf16"):
     """Reference attention for decode and prefill.
 
     q: uint16 bf16 bits [B, sq, Hq, d]; k, v: uint16 [B, S, Hkv, d].
@@ -88,12 +102,12 @@ def attention(q, k, v, seqlens=None, causal=True, row_block=512):
     for b in range(B):
         L = S if seqlens is None else int(min(max(int(seqlens[b]), 0), S))
         for g in range(Hkv):
-            kk = bf16_bits_to_f64(k[b, :L, g])
-            vv = bf16_bits_to_f64(v[b, :L, g])
+            kk = to_f64(k[b, :L, g], dtype)
+            vv = to_f64(v[b, :L, g], dtype)
             for t0 in range(0, sq, max(1, row_block // G)):
                 t1 = min(sq, t0 + max(1, row_block // G))
                 # rows ordered (t, head-in-group)
-                qr = bf16_bits_to_f64(q[b, t0:t1, g * G:(g + 1) * G]).reshape(-1, d)
+                qr = to_f64(q[b, t0:t1, g * G:(g + 1) * G], dtype).reshape(-1, d)
                 nv = np.array([_visible(L, sq, t, causal) for t in range(t0, t1)
                                for _ in range(G)], dtype=np.int64)
                 Lmax = int(nv.max()) if nv.size else 0
@@ -103,7 +117,7 @@ def attention(q, k, v, seqlens=None, causal=True, row_block=512):
     return O, LSE
 
 
-def attention_rows(q, k, v, rows, seqlens=None, causal=True):
+def attention_rows(q, k, v, rows, seqlens=None, causal=True, dtype="bf16"):
     """Reference O and LSE for selected (b, t, h) rows only (for large shapes).
 
     rows: iterable of (b, t, h). Returns (O [n, d], LSE [n]) in the given order.
@@ -118,14 +132,14 @@ def attention_rows(q, k, v, rows, seqlens=None, causal=True):
         L = S if seqlens is None else int(min(max(int(seqlens[b]), 0), S))
         n = _visible(L, sq, t, causal)
         g = h // G
-        qr = bf16_bits_to_f64(q[b, t, h]).reshape(1, d)
-        o, lse = _attend(qr, bf16_bits_to_f64(k[b, :n, g]), bf16_bits_to_f64(v[b, :n, g]),
+        qr = to_f64(q[b, t, h], dtype).reshape(1, d)
+        o, lse = _attend(qr, to_f64(k[b, :n, g], dtype), to_f64(v[b, :n, g], dtype),
                          np.array([n]), d)
         O[i], LSE[i] = o[0], lse[0]
     return O, LSE
 
 
-def probabilities(q, k, b, t, h, seqlens=None, causal=True):
+def probabilities(q, k, b, t, h, seqlens=None, causal=True, dtype="bf16"):
     """The softmax row P[b, h, t, :] over all S cache positions (zeros where masked)."""
     B, sq, Hq, d = q.shape
     S, Hkv = k.shape[1], k.shape[2]
@@ -135,7 +149,7 @@ def probabilities(q, k, b, t, h, seqlens=None, causal=True):
     out = np.zeros(S, dtype=np.float64)
     if n == 0:
         return out
-    s = bf16_bits_to_f64(k[b, :n, h // G]) @ bf16_bits_to_f64(q[b, t, h]) / math.sqrt(d)
+    s = to_f64(k[b, :n, h // G], dtype) @ to_f64(q[b, t, h], dtype) / math.sqrt(d)
     e = np.exp(s - s.max())
     out[:n] = e / e.sum()
     return out

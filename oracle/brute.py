@@ -16,8 +16,13 @@ def _bf16(x: int) -> float:
     return struct.unpack("<f", struct.pack("<I", (int(x) & 0xFFFF) << 16))[0]
 
 
-def brute_attention(q, k, v, seqlens=None, causal=True):
+def _f16(x: int) -> float:
+    return struct.unpack("<e", struct.pack("<H", int(x) & 0xFFFF))[0]
+
+
+def brute_attention(q, k, v, seqlens=None, causal=True, dtype="bf16"):
     """Nested-list result: O[b][t][h][e], LSE[b][h][t] (floats)."""
+    dec = {"bf16": _bf16, "f16": _f16}[dtype]
     B, sq, Hq, d = (int(x) for x in q.shape)
     S, Hkv = int(k.shape[1]), int(k.shape[2])
     G = Hq // Hkv
@@ -31,15 +36,15 @@ def brute_attention(q, k, v, seqlens=None, causal=True):
                 js = [j for j in range(L) if (not causal) or j <= L - sq + t]
                 if not js:
                     continue
-                qv = [_bf16(q[b, t, h, e]) for e in range(d)]
+                qv = [dec(q[b, t, h, e]) for e in range(d)]
                 sc = []
                 for j in js:
-                    dot = math.fsum(qv[e] * _bf16(k[b, j, g, e]) for e in range(d))
+                    dot = math.fsum(qv[e] * dec(k[b, j, g, e]) for e in range(d))
                     sc.append(dot / math.sqrt(d))
                 mx = max(sc)
                 ws = [math.exp(s - mx) for s in sc]
                 den = math.fsum(ws)
                 for e in range(d):
-                    O[b][t][h][e] = math.fsum(w * _bf16(v[b, j, g, e]) for w, j in zip(ws, js)) / den
+                    O[b][t][h][e] = math.fsum(w * dec(v[b, j, g, e]) for w, j in zip(ws, js)) / den
                 LSE[b][h][t] = mx + math.log(den)
     return O, LSE

@@ -258,3 +258,54 @@ def test_attention_rows_matches_full():
     for i, (b, t, h) in enumerate(rows):
         assert np.allclose(Or[i], O[b, t, h], atol=1e-14)
         assert (Lr[i] == LSE[b, h, t]) or abs(Lr[i] - LSE[b, h, t]) < 1e-14
+
+
+# --- fp16 (IEEE binary16) inputs ------------------------------------------------
+
+def _binary16_by_formula(p):
+    """Value of a binary16 pattern from its fields: (-1)^s * 2^(e-15) * (1 + m/1024),
+    subnormals 2^-14 * m/1024 (written out here, not taken from any library)."""
+    s, e, m = (p >> 15) & 1, (p >> 10) & 0x1F, p & 0x3FF
+    sign = -1.0 if s else 1.0
+    if e == 0:
+        return sign * 2.0 ** -14 * (m / 1024.0)
+    assert e != 31
+    return sign * 2.0 ** (e - 15) * (1.0 + m / 1024.0)
+
+
+@pytest.mark.parametrize("pattern", [0x3C00, 0xC000, 0x0001, 0x03FF, 0x0400, 0x7BFF, 0x3555, 0xB266, 0x0000, 0x8000])
+def test_f16_decoders_match_the_binary16_definition(pattern):
+    from oracle.brute import _f16
+    want = _binary16_by_formula(pattern)
+    assert oracle.f16_bits_to_f64(np.array([pattern], dtype=np.uint16))[0] == want
+    assert _f16(pattern) == want
+    assert oracle.to_f64(np.array([pattern], dtype=np.uint16), "f16")[0] == want
+
+
+def test_f16_generator_rounds_to_nearest_even():
+    def f(x):
+        return int(wl.f32_to_f16_bits(np.array([x], dtype=np.float32))[0])
+    assert f(1.0 + 2.0 ** -11) == 0x3C00        # tie -> even (1.0)
+    assert f(1.0 + 3 * 2.0 ** -11) == 0x3C02    # tie -> even (1 + 2^-9)
+    assert f(1.0 + 2.0 ** -11 + 2.0 ** -20) == 0x3C01  # above the tie
+    assert f(65504.0) == 0x7BFF
+
+
+def test_f16_brute_force_matches_vectorised_oracle():
+    x = wl.make_decode(2, 4, 2, 16, 3, 40, [40, 7], seed=23, pad=wl.BF16_ZERO, dtype="f16")
+    O, L = oracle.attention(x.q, x.k, x.v, x.seqlens, True, dtype="f16")
+    Ob, Lb = oracle.brute_attention(x.q, x.k, x.v, x.seqlens, True, dtype="f16")
+    assert np.abs(O - np.array(Ob)).max() <= 1e-12
+    assert np.abs(L - np.array(Lb)).max() <= 1e-12
+    # the same bits read as bf16 give a different result: the type is honoured
+    Ox, _ = oracle.attention(x.q, x.k, x.v, x.seqlens, True, dtype="bf16")
+    assert np.abs(O - Ox).max() > 1e-3
+
+
+def test_f16_one_hot_limit():
+    """A key equal to a large multiple of q dominates: O is that key's value row (fp16 exact)."""
+    x = wl.make_decode(1, 1, 1, 16, 1, 9, [9], seed=29, pad=wl.BF16_ZERO, dtype="f16")
+    qv = oracle.f16_bits_to_f64(x.q[0, 0, 0])
+    x.k[0, 4, 0] = wl.f32_to_f16_bits((8.0 * qv).astype(np.float32))
+    O, L = oracle.attention(x.q, x.k, x.v, x.seqlens, True, dtype="f16")
+    assert np.abs(O[0, 0, 0] - oracle.f16_bits_to_f64(x.v[0, 4, 0])).max() <= 1e-6

@@ -2,8 +2,9 @@
 
 This module holds no attention arithmetic. It fixes the five workload shapes,
 draws N(0, 1) float32 values from counter-keyed NumPy PCG64 streams, and rounds
-them to bfloat16 bit patterns (round to nearest, ties to even). Both the CPU
-oracle and the GPU path read the same uint16 bit patterns produced here.
+them to bfloat16 (default) or IEEE fp16 bit patterns (round to nearest, ties to
+even). Both the CPU oracle and the GPU path read the same uint16 bit patterns
+produced here.
 
 Recipe (deterministic, independent of thread count):
   * every tensor is cut into chunks of CHUNK elements in C order; chunk ``i``
@@ -28,6 +29,8 @@ CHUNK = 1 << 22
 TID_Q, TID_K, TID_V, TID_LEN = 1, 2, 3, 4
 BF16_NAN = np.uint16(0x7FC0)
 BF16_ZERO = np.uint16(0)
+F16_NAN = np.uint16(0x7E00)
+NAN_BITS = {"bf16": BF16_NAN, "f16": F16_NAN}
 
 
 def _threads() -> int:
@@ -45,15 +48,21 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     return ((u + r) >> 16).astype(np.uint16)
 
 
-def normal_bf16(seed: int, tid: int, n: int, sub: int = 0) -> np.ndarray:
-    """n bf16 bit patterns of N(0,1) draws from stream (seed, tid, sub)."""
+def f32_to_f16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to IEEE binary16 (nearest, ties to even); return uint16 bits."""
+    return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def normal_bits(seed: int, tid: int, n: int, sub: int = 0, dtype: str = "bf16") -> np.ndarray:
+    """n bit patterns (bf16, or fp16 with dtype="f16") of N(0,1) draws from stream (seed, tid, sub)."""
+    to_bits = {"bf16": f32_to_bf16_bits, "f16": f32_to_f16_bits}[dtype]
     out = np.empty(n, dtype=np.uint16)
     nchunks = (n + CHUNK - 1) // CHUNK
 
     def work(i: int) -> None:
         lo, hi = i * CHUNK, min(n, (i + 1) * CHUNK)
         g = np.random.default_rng(np.random.SeedSequence([seed, tid, sub, i]))
-        out[lo:hi] = f32_to_bf16_bits(g.standard_normal(hi - lo, dtype=np.float32))
+        out[lo:hi] = to_bits(g.standard_normal(hi - lo, dtype=np.float32))
 
     if nchunks <= 1:
         for i in range(nchunks):
@@ -62,6 +71,11 @@ def normal_bf16(seed: int, tid: int, n: int, sub: int = 0) -> np.ndarray:
         with ThreadPoolExecutor(_threads()) as ex:
             list(ex.map(work, range(nchunks)))
     return out
+
+
+def normal_bf16(seed: int, tid: int, n: int, sub: int = 0) -> np.ndarray:
+    """n bf16 bit patterns of N(0,1) draws from stream (seed, tid, sub)."""
+    return normal_bits(seed, tid, n, sub, "bf16")
 
 
 @dataclass(frozen=True)
@@ -120,6 +134,7 @@ class DecodeInputs:
     v: np.ndarray  # uint16 [B, S_max, Hkv, d]
     seqlens: np.ndarray  # int32 [B]
     meta: dict = field(default_factory=dict)
+    dtype: str = "bf16"  # element type of q, k, v: "bf16" or "f16"
 
 
 @dataclass
@@ -128,6 +143,7 @@ class PrefillInputs:
     k: np.ndarray  # uint16 [B, S, Hkv, d]
     v: np.ndarray  # uint16 [B, S, Hkv, d]
     meta: dict = field(default_factory=dict)
+    dtype: str = "bf16"
 
 
 def draw_lengths(seed: int, batch: int, lo: int, hi: int) -> np.ndarray:
@@ -138,10 +154,15 @@ def draw_lengths(seed: int, batch: int, lo: int, hi: int) -> np.ndarray:
 
 
 def make_decode(batch, n_q_heads, n_kv_heads, d, seqlen_q, max_seqlen_k, seqlens,
-                seed, pad=BF16_NAN) -> DecodeInputs:
-    """Decode inputs of an arbitrary shape with given per-sequence lengths."""
+                seed, pad=None, dtype="bf16") -> DecodeInputs:
+    """Decode inputs of an arbitrary shape with given per-sequence lengths.
+
+    pad: bit pattern of the cache rows past each sequence end (default: NaN of
+    the element type)."""
+    if pad is None:
+        pad = NAN_BITS[dtype]
     seqlens = np.asarray(seqlens, dtype=np.int32).reshape(batch)
-    q = normal_bf16(seed, TID_Q, batch * seqlen_q * n_q_heads * d).reshape(
+    q = normal_bits(seed, TID_Q, batch * seqlen_q * n_q_heads * d, dtype=dtype).reshape(
         batch, seqlen_q, n_q_heads, d)
     k = np.full((batch, max_seqlen_k, n_kv_heads, d), pad, dtype=np.uint16)
     v = np.full((batch, max_seqlen_k, n_kv_heads, d), pad, dtype=np.uint16)
@@ -150,12 +171,12 @@ def make_decode(batch, n_q_heads, n_kv_heads, d, seqlen_q, max_seqlen_k, seqlens
         L = int(min(max(seqlens[b], 0), max_seqlen_k))
         if L == 0:
             continue
-        k[b, :L] = normal_bf16(seed, TID_K, L * row, sub=b).reshape(L, n_kv_heads, d)
-        v[b, :L] = normal_bf16(seed, TID_V, L * row, sub=b).reshape(L, n_kv_heads, d)
-    return DecodeInputs(q, k, v, seqlens, dict(seed=seed))
+        k[b, :L] = normal_bits(seed, TID_K, L * row, sub=b, dtype=dtype).reshape(L, n_kv_heads, d)
+        v[b, :L] = normal_bits(seed, TID_V, L * row, sub=b, dtype=dtype).reshape(L, n_kv_heads, d)
+    return DecodeInputs(q, k, v, seqlens, dict(seed=seed), dtype)
 
 
-def decode_inputs(cfg: DecodeConfig | str, pad=BF16_NAN) -> DecodeInputs:
+def decode_inputs(cfg: DecodeConfig | str, pad=None) -> DecodeInputs:
     if isinstance(cfg, str):
         cfg = DECODE_CONFIGS[cfg]
     lens = draw_lengths(cfg.seed, cfg.batch, cfg.len_lo, cfg.len_hi)
@@ -165,14 +186,15 @@ def decode_inputs(cfg: DecodeConfig | str, pad=BF16_NAN) -> DecodeInputs:
     return out
 
 
-def make_prefill(batch, n_q_heads, n_kv_heads, d, seqlen_q, seqlen_k, seed) -> PrefillInputs:
-    q = normal_bf16(seed, TID_Q, batch * seqlen_q * n_q_heads * d).reshape(
+def make_prefill(batch, n_q_heads, n_kv_heads, d, seqlen_q, seqlen_k, seed,
+                 dtype="bf16") -> PrefillInputs:
+    q = normal_bits(seed, TID_Q, batch * seqlen_q * n_q_heads * d, dtype=dtype).reshape(
         batch, seqlen_q, n_q_heads, d)
-    k = normal_bf16(seed, TID_K, batch * seqlen_k * n_kv_heads * d).reshape(
+    k = normal_bits(seed, TID_K, batch * seqlen_k * n_kv_heads * d, dtype=dtype).reshape(
         batch, seqlen_k, n_kv_heads, d)
-    v = normal_bf16(seed, TID_V, batch * seqlen_k * n_kv_heads * d).reshape(
+    v = normal_bits(seed, TID_V, batch * seqlen_k * n_kv_heads * d, dtype=dtype).reshape(
         batch, seqlen_k, n_kv_heads, d)
-    return PrefillInputs(q, k, v, dict(seed=seed))
+    return PrefillInputs(q, k, v, dict(seed=seed), dtype)
 
 
 def prefill_inputs(cfg: PrefillConfig | str) -> PrefillInputs:
