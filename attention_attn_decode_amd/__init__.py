@@ -27,7 +27,7 @@ ATTN_MAX_BATCH = 8192
 
 # Every symbol include/attn.h declares.
 EXPORTS = ("attn_decode_plan", "attn_decode_workspace_size", "attn_decode", "attn_decode_ex",
-           "attn_fwd", "attn_status_string", "attn_version")
+           "attn_decode_f16", "attn_fwd", "attn_fwd_f16", "attn_status_string", "attn_version")
 
 _lib = None
 
@@ -55,10 +55,12 @@ def lib() -> ctypes.CDLL:
     dec = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, sz, vp]
     L.attn_decode.argtypes = dec
     L.attn_decode.restype = i32
-    L.attn_decode_ex.argtypes = dec + [i32]
-    L.attn_decode_ex.restype = i32
-    L.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp]
-    L.attn_fwd.restype = i32
+    for name in ("attn_decode_ex", "attn_decode_f16"):
+        getattr(L, name).argtypes = dec + [i32]
+        getattr(L, name).restype = i32
+    for name in ("attn_fwd", "attn_fwd_f16"):
+        getattr(L, name).argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp]
+        getattr(L, name).restype = i32
     L.attn_status_string.argtypes = [i32]
     L.attn_status_string.restype = ctypes.c_char_p
     L.attn_version.argtypes = []
@@ -118,21 +120,32 @@ def _check(t, name, dtype, ndim=None):
         raise ValueError(f"{name} must have {ndim} dimensions")
 
 
+def _elem(q):
+    """Entry-point suffix for the element type of q (bf16 or fp16)."""
+    import torch
+    if q.dtype == torch.bfloat16:
+        return torch.bfloat16, False
+    if q.dtype == torch.float16:
+        return torch.float16, True
+    raise TypeError(f"q must be bfloat16 or float16, got {q.dtype}")
+
+
 def attn_decode(q, k_cache, v_cache, seqlens_k, o, lse=None, workspace=None, num_splits=0,
                 stream=None):
     """GQA KV-cache decode; sizes are read from the tensor shapes.
 
-    q, o: bf16 [B, sq, Hq, d]; k_cache, v_cache: bf16 [B, S_max, Hkv, d];
+    q, o: bf16 or fp16 [B, sq, Hq, d]; k_cache, v_cache: same type [B, S_max, Hkv, d];
     seqlens_k: int32 [B]; lse: fp32 [B, Hq, sq] or None; workspace: a uint8 (or
     any) device tensor of at least attn_decode_workspace_size(...) bytes for the
     same num_splits, or None for one piece per KV head.
     """
     import torch
-    _check(q, "q", torch.bfloat16, 4)
-    _check(k_cache, "k_cache", torch.bfloat16, 4)
-    _check(v_cache, "v_cache", torch.bfloat16, 4)
+    et, f16 = _elem(q)
+    _check(q, "q", et, 4)
+    _check(k_cache, "k_cache", et, 4)
+    _check(v_cache, "v_cache", et, 4)
     _check(seqlens_k, "seqlens_k", torch.int32, 1)
-    _check(o, "o", torch.bfloat16, 4)
+    _check(o, "o", et, 4)
     B, sq, Hq, d = q.shape
     _, S, Hkv, dk = k_cache.shape
     if tuple(v_cache.shape) != tuple(k_cache.shape) or dk != d or k_cache.shape[0] != B:
@@ -148,18 +161,20 @@ def attn_decode(q, k_cache, v_cache, seqlens_k, o, lse=None, workspace=None, num
         if not workspace.is_cuda or not workspace.is_contiguous():
             raise ValueError("workspace must be contiguous device memory")
         wbytes = workspace.numel() * workspace.element_size()
-    st = lib().attn_decode_ex(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens_k), _ptr(o),
-                              _ptr(lse), Hq, Hkv, d, sq, B, S, _ptr(workspace), wbytes,
-                              _stream_ptr(stream), int(num_splits))
+    fn = lib().attn_decode_f16 if f16 else lib().attn_decode_ex
+    st = fn(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens_k), _ptr(o), _ptr(lse), Hq, Hkv, d, sq, B, S,
+            _ptr(workspace), wbytes, _stream_ptr(stream), int(num_splits))
     if st != ATTN_OK:
         raise AttnError(st, "attn_decode")
 
 
 def attn_fwd(q, k, v, o, lse=None, causal=True, stream=None):
-    """Prefill forward. q, o: bf16 [B, Sq, Hq, d]; k, v: bf16 [B, Sk, Hkv, d]; lse fp32 [B, Hq, Sq]."""
+    """Prefill forward. q, o: bf16 or fp16 [B, Sq, Hq, d]; k, v: same type [B, Sk, Hkv, d];
+    lse fp32 [B, Hq, Sq]."""
     import torch
+    et, f16 = _elem(q)
     for t, nm in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
-        _check(t, nm, torch.bfloat16, 4)
+        _check(t, nm, et, 4)
     B, Sq, Hq, d = q.shape
     _, Sk, Hkv, dk = k.shape
     if tuple(v.shape) != tuple(k.shape) or dk != d or k.shape[0] != B or tuple(o.shape) != tuple(q.shape):
@@ -168,7 +183,8 @@ def attn_fwd(q, k, v, o, lse=None, causal=True, stream=None):
         _check(lse, "lse", torch.float32, 3)
         if tuple(lse.shape) != (B, Hq, Sq):
             raise ValueError("lse must be [B, Hq, Sq]")
-    st = lib().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), 1 if causal else 0,
-                        B, Sq, Sk, Hq, Hkv, d, _stream_ptr(stream))
+    fn = lib().attn_fwd_f16 if f16 else lib().attn_fwd
+    st = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), 1 if causal else 0, B, Sq, Sk, Hq, Hkv, d,
+            _stream_ptr(stream))
     if st != ATTN_OK:
         raise AttnError(st, "attn_fwd")

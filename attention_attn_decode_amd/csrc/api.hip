@@ -13,9 +13,9 @@ hipError_t launch_decode(const void *q, const void *k, const void *v, const int3
                          void *o, float *lse, float *ws_o, float2 *ws_ml, long long *meta,
                          int batch, int Hq,
                          int Hkv, int d, int sq, int max_len, int pieces, int min_piece,
-                         float scale_log2, hipStream_t stream);
+                         float scale_log2, bool f16, hipStream_t stream);
 hipError_t launch_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int causal,
-                      int batch, int Sq, int Sk, int Hq, int Hkv, int d, float scale_log2,
+                      int batch, int Sq, int Sk, int Hq, int Hkv, int d, float scale_log2, bool f16,
                       hipStream_t stream);
 }  // namespace attn
 
@@ -82,10 +82,14 @@ size_t attn_decode_workspace_size(int batch, int n_q_heads, int n_kv_heads, int 
   return workspace_bytes_for(batch, n_kv_heads, d, plan_pieces(n_kv_heads, d, num_splits));
 }
 
-int attn_decode_ex(const void *q, const void *k_cache, const void *v_cache,
-                   const int32_t *seqlens_k, void *o, float *lse, int n_q_heads, int n_kv_heads,
-                   int d, int seqlen_q, int batch, int max_seqlen_k, void *workspace,
-                   size_t workspace_bytes, void *stream, int num_splits) {
+}  // extern "C"
+
+namespace {
+
+int decode_impl(const void *q, const void *k_cache, const void *v_cache, const int32_t *seqlens_k,
+                void *o, float *lse, int n_q_heads, int n_kv_heads, int d, int seqlen_q, int batch,
+                int max_seqlen_k, void *workspace, size_t workspace_bytes, void *stream,
+                int num_splits, bool f16) {
   if (!q || !k_cache || !v_cache || !seqlens_k || !o || num_splits < 0) return ATTN_ERR_INVALID;
   const int st = check_decode_shape(n_q_heads, n_kv_heads, d, seqlen_q, batch, max_seqlen_k);
   if (st != ATTN_OK) return st;
@@ -108,9 +112,46 @@ int attn_decode_ex(const void *q, const void *k_cache, const void *v_cache,
   }
   const hipError_t err = attn::launch_decode(
       q, k_cache, v_cache, seqlens_k, o, lse, ws_o, ws_ml, meta, batch, n_q_heads, n_kv_heads, d,
-      seqlen_q, max_seqlen_k, pieces, ATTN_MIN_PIECE, scale_log2_for(d),
+      seqlen_q, max_seqlen_k, pieces, ATTN_MIN_PIECE, scale_log2_for(d), f16,
       static_cast<hipStream_t>(stream));
   return err == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+int fwd_impl(const void *q, const void *k, const void *v, void *o, float *lse, int causal, int batch,
+             int seqlen_q, int seqlen_k, int n_q_heads, int n_kv_heads, int d, void *stream, bool f16) {
+  if (!q || !k || !v || !o) return ATTN_ERR_INVALID;
+  if (batch <= 0 || seqlen_q <= 0 || seqlen_k <= 0 || n_q_heads <= 0 || n_kv_heads <= 0)
+    return ATTN_ERR_INVALID;
+  if (n_q_heads % n_kv_heads != 0) return ATTN_ERR_INVALID;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  const long wgs = (long)((seqlen_q + 255) / 256) * batch * n_q_heads;  // 256-row query tiles
+  if (wgs > 0x7fffffffL) return ATTN_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (lse && !aligned4(lse)))
+    return ATTN_ERR_MISALIGNED;
+  const hipError_t err =
+      attn::launch_fwd(q, k, v, o, lse, causal ? 1 : 0, batch, seqlen_q, seqlen_k, n_q_heads,
+                       n_kv_heads, d, scale_log2_for(d), f16, static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_decode_ex(const void *q, const void *k_cache, const void *v_cache,
+                   const int32_t *seqlens_k, void *o, float *lse, int n_q_heads, int n_kv_heads,
+                   int d, int seqlen_q, int batch, int max_seqlen_k, void *workspace,
+                   size_t workspace_bytes, void *stream, int num_splits) {
+  return decode_impl(q, k_cache, v_cache, seqlens_k, o, lse, n_q_heads, n_kv_heads, d, seqlen_q, batch,
+                     max_seqlen_k, workspace, workspace_bytes, stream, num_splits, false);
+}
+
+int attn_decode_f16(const void *q, const void *k_cache, const void *v_cache,
+                    const int32_t *seqlens_k, void *o, float *lse, int n_q_heads, int n_kv_heads,
+                    int d, int seqlen_q, int batch, int max_seqlen_k, void *workspace,
+                    size_t workspace_bytes, void *stream, int num_splits) {
+  return decode_impl(q, k_cache, v_cache, seqlens_k, o, lse, n_q_heads, n_kv_heads, d, seqlen_q, batch,
+                     max_seqlen_k, workspace, workspace_bytes, stream, num_splits, true);
 }
 
 int attn_decode(const void *q, const void *k_cache, const void *v_cache, const int32_t *seqlens_k,
@@ -123,19 +164,13 @@ int attn_decode(const void *q, const void *k_cache, const void *v_cache, const i
 int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int causal,
              int batch, int seqlen_q, int seqlen_k, int n_q_heads, int n_kv_heads, int d,
              void *stream) {
-  if (!q || !k || !v || !o) return ATTN_ERR_INVALID;
-  if (batch <= 0 || seqlen_q <= 0 || seqlen_k <= 0 || n_q_heads <= 0 || n_kv_heads <= 0)
-    return ATTN_ERR_INVALID;
-  if (n_q_heads % n_kv_heads != 0) return ATTN_ERR_INVALID;
-  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
-  const long wgs = (long)((seqlen_q + 255) / 256) * batch * n_q_heads;  // 256-row query tiles
-  if (wgs > 0x7fffffffL) return ATTN_ERR_UNSUPPORTED;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (lse && !aligned4(lse)))
-    return ATTN_ERR_MISALIGNED;
-  const hipError_t err =
-      attn::launch_fwd(q, k, v, o, lse, causal ? 1 : 0, batch, seqlen_q, seqlen_k, n_q_heads,
-                       n_kv_heads, d, scale_log2_for(d), static_cast<hipStream_t>(stream));
-  return err == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+  return fwd_impl(q, k, v, o, lse, causal, batch, seqlen_q, seqlen_k, n_q_heads, n_kv_heads, d, stream, false);
+}
+
+int attn_fwd_f16(const void *q, const void *k, const void *v, void *o, float *lse, int causal,
+                 int batch, int seqlen_q, int seqlen_k, int n_q_heads, int n_kv_heads, int d,
+                 void *stream) {
+  return fwd_impl(q, k, v, o, lse, causal, batch, seqlen_q, seqlen_k, n_q_heads, n_kv_heads, d, stream, true);
 }
 
 const char *attn_status_string(int status) {

@@ -33,12 +33,50 @@ __device__ __forceinline__ f32x16 mfma_32x32x16(const uint4 &a, const uint4 &b, 
                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// Element-type dispatch for the kernels: F16 = false for bfloat16 inputs,
+// true for IEEE fp16 inputs. The MFMA operand and accumulator layouts are the
+// same for both types; only the instruction and the P/O conversion differ.
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+
+template <bool F16>
+__device__ __forceinline__ f32x4 mma16(const uint4 &a, const uint4 &b, f32x4 c) {
+  if constexpr (F16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                   0, 0);
+  else
+    return mfma_16x16x32(a, b, c);
+}
+
+template <bool F16>
+__device__ __forceinline__ f32x16 mma32(const uint4 &a, const uint4 &b, f32x16 c) {
+  if constexpr (F16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                   0, 0);
+  else
+    return mfma_32x32x16(a, b, c);
+}
+
 // Two floats -> packed bf16x2, round to nearest even (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   bf16x2 v;
   v[0] = (__bf16)lo;
   v[1] = (__bf16)hi;
   return __builtin_bit_cast(uint32_t, v);
+}
+
+// Two floats -> the packed pair of the element type, round to nearest even
+// (v_cvt_pk_bf16_f32 or v_cvt_pk_f16_f32).
+template <bool F16>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  if constexpr (F16) {
+    f16x2 v;
+    v[0] = (_Float16)lo;
+    v[1] = (_Float16)hi;
+    return __builtin_bit_cast(uint32_t, v);
+  } else {
+    return pack_bf16x2(lo, hi);
+  }
 }
 
 // 2^x on the transcendental unit (v_exp_f32); 2^-inf = 0.

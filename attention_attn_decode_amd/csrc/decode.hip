@@ -184,7 +184,7 @@ struct Slot {
   uint4 q[KST];
 };
 
-template <int D>
+template <int D, bool F16>
 __global__ void __launch_bounds__(256, 1)
 decode_stream(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
               const uint16_t *__restrict__ vc, const int *__restrict__ seqlens,
@@ -286,7 +286,7 @@ decode_stream(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
 #pragma unroll
       for (int kk = 0; kk < KST; ++kk) {
         const int c = 4 * kk + gq;
-        sacc[t] = mfma_16x16x32(lds16(klds + r * D + ((c ^ k_swz<D>(r)) * 8)), sl.q[kk], sacc[t]);
+        sacc[t] = mma16<F16>(lds16(klds + r * D + ((c ^ k_swz<D>(r)) * 8)), sl.q[kk], sacc[t]);
       }
     }
 
@@ -323,8 +323,8 @@ decode_stream(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
     // on three gates).
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) oacc[mt] *= alpha;
-    const uint4 pop = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                                 pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7]));
+    const uint4 pop = make_uint4(pack2<F16>(p[0], p[1]), pack2<F16>(p[2], p[3]),
+                                 pack2<F16>(p[4], p[5]), pack2<F16>(p[6], p[7]));
     // A operand: the same eight keys 8gq .. 8gq + 7 at column 16mt + (lane % 16),
     // as two transposed 4-key reads.
     const int trk = lane & 15;
@@ -337,7 +337,7 @@ decode_stream(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
         const int c = 2 * mt + ((trk & 3) >> 1);
         tr[uu] = lds_tr4(vlds + r * D + ((c ^ v_swz<D>(r)) * 8) + 4 * (trk & 1));
       }
-      oacc[mt] = mfma_16x16x32(make_uint4(tr[0].x, tr[0].y, tr[1].x, tr[1].y), pop, oacc[mt]);
+      oacc[mt] = mma16<F16>(make_uint4(tr[0].x, tr[0].y, tr[1].x, tr[1].y), pop, oacc[mt]);
     }
     wave_lds_sync();
   };
@@ -357,8 +357,8 @@ decode_stream(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
           *reinterpret_cast<uint2 *>(dst + 16 * mt + 4 * gq) =
-              make_uint2(pack_bf16x2(oacc[mt][0] * inv, oacc[mt][1] * inv),
-                         pack_bf16x2(oacc[mt][2] * inv, oacc[mt][3] * inv));
+              make_uint2(pack2<F16>(oacc[mt][0] * inv, oacc[mt][1] * inv),
+                         pack2<F16>(oacc[mt][2] * inv, oacc[mt][3] * inv));
         if (lse != nullptr && gq == 0)
           lse[((size_t)b * Hq + head) * sq + tn] = l_col > 0.f ? kLn2 * (m_run + __log2f(l_col)) : kNegInf;
       }
@@ -437,7 +437,7 @@ decode_stream(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
 // idle threads form extra groups that merge disjoint, fixed subsets of the
 // pieces (w = w0 + grp, w0 + grp + NG, ...), folded together at the end in
 // group order: the result does not depend on timing.
-template <int D>
+template <int D, bool F16>
 __global__ void __launch_bounds__(256)
 combine_pieces(const float *__restrict__ ws_o, const float2 *__restrict__ ws_ml,
                const long long *__restrict__ meta, const int *__restrict__ seqlens,
@@ -525,7 +525,7 @@ combine_pieces(const float *__restrict__ ws_o, const float2 *__restrict__ ws_ml,
   uint16_t *dst = o + ((size_t)(b * sq + ct) * Hq + chead) * D + seg;
 #pragma unroll
   for (int e = 0; e < SEG; e += 2)
-    *reinterpret_cast<uint32_t *>(dst + e) = pack_bf16x2(acc[e] * inv, acc[e + 1] * inv);
+    *reinterpret_cast<uint32_t *>(dst + e) = pack2<F16>(acc[e] * inv, acc[e + 1] * inv);
   if (lse != nullptr && (tid & 15) == 0)
     lse[((size_t)b * Hq + chead) * sq + ct] = lsum > 0.f ? kLn2 * (M + __log2f(lsum)) : kNegInf;
   (void)s_m;
@@ -541,7 +541,7 @@ hipError_t launch_decode(const void *q, const void *k, const void *v, const int3
                          void *o, float *lse, float *ws_o, float2 *ws_ml, long long *meta,
                          int batch, int Hq,
                          int Hkv, int d, int sq, int max_len, int pieces, int min_piece,
-                         float scale_log2, hipStream_t stream) {
+                         float scale_log2, bool f16, hipStream_t stream) {
   const dim3 block(256);
   const dim3 grid((unsigned)(((long)Hkv * pieces + kWaves - 1) / kWaves));
   const int min_units = min_piece > kSub ? min_piece / kSub : 1;
@@ -549,23 +549,33 @@ hipError_t launch_decode(const void *q, const void *k, const void *v, const int3
   const auto *kk = static_cast<const uint16_t *>(k);
   const auto *vv = static_cast<const uint16_t *>(v);
   auto *oo = static_cast<uint16_t *>(o);
-  if (d == 128)
-    hipLaunchKernelGGL((decode_stream<128>), grid, block, 0, stream, qq, kk, vv, seqlens, oo, lse,
-                       ws_o, ws_ml, meta, batch, Hq, Hkv, sq, max_len, pieces, min_units, scale_log2);
-  else
-    hipLaunchKernelGGL((decode_stream<64>), grid, block, 0, stream, qq, kk, vv, seqlens, oo, lse,
-                       ws_o, ws_ml, meta, batch, Hq, Hkv, sq, max_len, pieces, min_units, scale_log2);
+  auto split = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, block, 0, stream, qq, kk, vv, seqlens, oo, lse, ws_o, ws_ml, meta, batch, Hq,
+                       Hkv, sq, max_len, pieces, min_units, scale_log2);
+  };
+  if (d == 128) {
+    if (f16) split(decode_stream<128, true>);
+    else split(decode_stream<128, false>);
+  } else {
+    if (f16) split(decode_stream<64, true>);
+    else split(decode_stream<64, false>);
+  }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   // Launched even with one piece per KV head: it writes O = 0 and LSE = -inf
   // for empty sequences, which no split-kernel wave visits.
   const dim3 cgrid(batch, Hkv);
-  if (d == 128)
-    hipLaunchKernelGGL(combine_pieces<128>, cgrid, block, 0, stream, ws_o, ws_ml, meta, seqlens, oo,
-                       lse, batch, Hq, Hkv, sq, max_len, pieces, min_units);
-  else
-    hipLaunchKernelGGL(combine_pieces<64>, cgrid, block, 0, stream, ws_o, ws_ml, meta, seqlens, oo,
-                       lse, batch, Hq, Hkv, sq, max_len, pieces, min_units);
+  auto combine = [&](auto kern) {
+    hipLaunchKernelGGL(kern, cgrid, block, 0, stream, ws_o, ws_ml, meta, seqlens, oo, lse, batch, Hq, Hkv, sq,
+                       max_len, pieces, min_units);
+  };
+  if (d == 128) {
+    if (f16) combine(combine_pieces<128, true>);
+    else combine(combine_pieces<128, false>);
+  } else {
+    if (f16) combine(combine_pieces<64, true>);
+    else combine(combine_pieces<64, false>);
+  }
   return hipGetLastError();
 }
 

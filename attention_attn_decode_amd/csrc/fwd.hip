@@ -72,7 +72,7 @@ template <int D> struct VRow { static constexpr int v = D == 128 ? 160 : 96; };
 // stages V, each during its VALU phase, one block ahead of use.
 constexpr int kBMP = 256;  // query rows per work-group
 
-template <int D>
+template <int D, bool F16>
 __global__ void __launch_bounds__(512, 1)
 fwd_pp(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
        const uint16_t *__restrict__ v, uint16_t *__restrict__ o, float *__restrict__ lse,
@@ -169,7 +169,7 @@ fwd_pp(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
 #pragma unroll
       for (int r = 0; r < 16; ++r) S[t][r] = 0.f;
 #pragma unroll
-      for (int kk = 0; kk < KST; ++kk) S[t] = mfma_32x32x16(lds16(kl + 32 * t * KROW + 16 * kk), qop[kk], S[t]);
+      for (int kk = 0; kk < KST; ++kk) S[t] = mma32<F16>(lds16(kl + 32 * t * KROW + 16 * kk), qop[kk], S[t]);
     }
   };
   auto pv = [&](int slot) {
@@ -180,7 +180,7 @@ fwd_pp(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
       for (int ks = 0; ks < NKS; ++ks) {
         const uint2 t0 = lds_tr4(vl + 16 * ks * VROW + 32 * mt);
         const uint2 t1 = lds_tr4(vl + (16 * ks + 4) * VROW + 32 * mt);
-        oacc[mt] = mfma_32x32x16(make_uint4(t0.x, t0.y, t1.x, t1.y), pop[ks], oacc[mt]);
+        oacc[mt] = mma32<F16>(make_uint4(t0.x, t0.y, t1.x, t1.y), pop[ks], oacc[mt]);
       }
   };
   // Softmax of block j0 (register r of score tile t holds key
@@ -214,8 +214,8 @@ fwd_pp(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
           pv8[s2] = exp2_hw(__builtin_fmaf(S[t][8 * hh + s2], scale_log2, -m_use));
           psum += pv8[s2];
         }
-        pop[2 * t + hh] = make_uint4(pack_bf16x2(pv8[0], pv8[1]), pack_bf16x2(pv8[2], pv8[3]),
-                                     pack_bf16x2(pv8[4], pv8[5]), pack_bf16x2(pv8[6], pv8[7]));
+        pop[2 * t + hh] = make_uint4(pack2<F16>(pv8[0], pv8[1]), pack2<F16>(pv8[2], pv8[3]),
+                                     pack2<F16>(pv8[4], pv8[5]), pack2<F16>(pv8[6], pv8[7]));
       }
     const float alpha = exp2_hw(fmaxf(m_run - m_new, -1e30f));
     l_run = l_run * alpha + psum;
@@ -263,11 +263,11 @@ fwd_pp(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
       if constexpr (g == 6) load_blk(j + 2 - G);
       if constexpr (g < NPV) {
         constexpr int ks = g / MT, mt = g % MT;
-        oacc[mt] = mfma_32x32x16(a, pop[ks], oacc[mt]);
+        oacc[mt] = mma32<F16>(a, pop[ks], oacc[mt]);
       } else {
         constexpr int m = g - NPV, t = m % NT, kk = m / NT;
-        if constexpr (kk == 0) S[t] = mfma_32x32x16(a, qop[kk], f32x16{});
-        else S[t] = mfma_32x32x16(a, qop[kk], S[t]);
+        if constexpr (kk == 0) S[t] = mma32<F16>(a, qop[kk], f32x16{});
+        else S[t] = mma32<F16>(a, qop[kk], S[t]);
       }
       __builtin_amdgcn_sched_barrier(0);
     });
@@ -348,8 +348,8 @@ fwd_pp(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     for (int a = 0; a < 4; ++a) {
       const int dd = 32 * mt + 8 * a + 4 * hl;
       *reinterpret_cast<uint2 *>(dst + dd) =
-          make_uint2(pack_bf16x2(oacc[mt][4 * a] * inv, oacc[mt][4 * a + 1] * inv),
-                     pack_bf16x2(oacc[mt][4 * a + 2] * inv, oacc[mt][4 * a + 3] * inv));
+          make_uint2(pack2<F16>(oacc[mt][4 * a] * inv, oacc[mt][4 * a + 1] * inv),
+                     pack2<F16>(oacc[mt][4 * a + 2] * inv, oacc[mt][4 * a + 3] * inv));
     }
   if (lse != nullptr && hl == 0)
     lse[((size_t)b * Hq + h) * Sq + qrow] = l_col > 0.f ? kLn2 * (m_run + __log2f(l_col)) : kNegInf;
@@ -358,7 +358,7 @@ fwd_pp(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
 }  // namespace
 
 hipError_t launch_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int causal,
-                      int batch, int Sq, int Sk, int Hq, int Hkv, int d, float scale_log2,
+                      int batch, int Sq, int Sk, int Hq, int Hkv, int d, float scale_log2, bool f16,
                       hipStream_t stream) {
   const int BH = batch * Hq;
   const int n_mblocks = (Sq + kBMP - 1) / kBMP;
@@ -367,12 +367,17 @@ hipError_t launch_fwd(const void *q, const void *k, const void *v, void *o, floa
   const auto *kk = static_cast<const uint16_t *>(k);
   const auto *vv = static_cast<const uint16_t *>(v);
   auto *oo = static_cast<uint16_t *>(o);
-  if (d == 128)
-    hipLaunchKernelGGL((fwd_pp<128>), grid, block, 0, stream, qq, kk, vv, oo, lse, Sq, Sk, Hq, Hkv, causal,
-                       scale_log2, n_mblocks, BH);
-  else
-    hipLaunchKernelGGL((fwd_pp<64>), grid, block, 0, stream, qq, kk, vv, oo, lse, Sq, Sk, Hq, Hkv, causal,
-                       scale_log2, n_mblocks, BH);
+  auto run = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, block, 0, stream, qq, kk, vv, oo, lse, Sq, Sk, Hq, Hkv, causal, scale_log2,
+                       n_mblocks, BH);
+  };
+  if (d == 128) {
+    if (f16) run(fwd_pp<128, true>);
+    else run(fwd_pp<128, false>);
+  } else {
+    if (f16) run(fwd_pp<64, true>);
+    else run(fwd_pp<64, false>);
+  }
   return hipGetLastError();
 }
 

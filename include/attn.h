@@ -17,9 +17,13 @@
  *
  * Conventions shared by all calls
  *   - Element types: Q, K, V, O are bfloat16 (passed as raw 16-bit patterns);
- *     LSE is float32. Softmax and accumulation run in fp32; P is rounded to
- *     bf16 (nearest even) before the P*V product; O is rounded to bf16 (nearest
- *     even) once, at the end.
+ *     the *_f16 entry points take IEEE fp16 instead, with the same layouts
+ *     ([GQA-SM100] checks its decode kernel in BF16 and FP16; the correctness
+ *     test of [FA4-edges] §Does it actually compute attention? runs fp16).
+ *     LSE is float32.
+ *     Softmax and accumulation run in fp32; P is rounded to the element type
+ *     (nearest even) before the P*V product; O is rounded to the element type
+ *     (nearest even) once, at the end.
  *   - Layouts are dense, row-major, with the head dimension d innermost:
  *       q, o          [batch][seqlen_q][n_q_heads][d]
  *       k, v (cache)  [batch][seq capacity][n_kv_heads][d]
@@ -144,6 +148,14 @@ int attn_decode_ex(const void *q, const void *k_cache, const void *v_cache,
                    void *workspace, size_t workspace_bytes, void *stream,
                    int num_splits);
 
+/* attn_decode_ex for IEEE fp16 q, k_cache, v_cache and o (same layouts, plan,
+ * workspace and errors). */
+int attn_decode_f16(const void *q, const void *k_cache, const void *v_cache,
+                    const int32_t *seqlens_k, void *o, float *lse, int n_q_heads,
+                    int n_kv_heads, int d, int seqlen_q, int batch, int max_seqlen_k,
+                    void *workspace, size_t workspace_bytes, void *stream,
+                    int num_splits);
+
 /*
  * Prefill forward ([FA4-edges] §Edge 1 · causal masking, §Edge 3 · tile
  * scheduling): q [batch][seqlen_q][n_q_heads][d], k and v
@@ -156,6 +168,11 @@ int attn_decode_ex(const void *q, const void *k_cache, const void *v_cache,
 int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int causal,
              int batch, int seqlen_q, int seqlen_k, int n_q_heads, int n_kv_heads, int d,
              void *stream);
+
+/* attn_fwd for IEEE fp16 q, k, v and o (same layouts and errors). */
+int attn_fwd_f16(const void *q, const void *k, const void *v, void *o, float *lse, int causal,
+                 int batch, int seqlen_q, int seqlen_k, int n_q_heads, int n_kv_heads, int d,
+                 void *stream);
 
 /* Static description of a status code; never NULL. */
 const char *attn_status_string(int status);

@@ -19,9 +19,15 @@ def torch():
     return _t
 
 
-def dev_bf16(bits: np.ndarray):
+def _tdtype(dtype):
     t = torch()
-    return t.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(t.bfloat16).cuda()
+    return {"bf16": t.bfloat16, "f16": t.float16}[dtype]
+
+
+def dev_bf16(bits: np.ndarray, dtype: str = "bf16"):
+    """Device tensor of the generator's 16-bit patterns, as bf16 (default) or fp16."""
+    t = torch()
+    return t.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(_tdtype(dtype)).cuda()
 
 
 def dev_i32(x):
@@ -33,9 +39,9 @@ def host_f64(t):
     return t.detach().double().cpu().numpy()
 
 
-def nan_like_bf16(shape):
+def nan_like_bf16(shape, dtype: str = "bf16"):
     t = torch()
-    return t.full(shape, float("nan"), dtype=t.bfloat16, device="cuda")
+    return t.full(shape, float("nan"), dtype=_tdtype(dtype), device="cuda")
 
 
 def nan_f32(shape):

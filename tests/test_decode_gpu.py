@@ -27,9 +27,9 @@ def run_decode(aa, x, num_splits=0, workspace="auto", poison=True):
     torch = G.torch()
     B, sq, Hq, d = x.q.shape
     S, Hkv = x.k.shape[1], x.k.shape[2]
-    q, k, v = G.dev_bf16(x.q), G.dev_bf16(x.k), G.dev_bf16(x.v)
+    q, k, v = G.dev_bf16(x.q, x.dtype), G.dev_bf16(x.k, x.dtype), G.dev_bf16(x.v, x.dtype)
     sl = G.dev_i32(x.seqlens)
-    o = G.nan_like_bf16((B, sq, Hq, d)) if poison else torch.empty((B, sq, Hq, d), dtype=torch.bfloat16, device="cuda")
+    o = G.nan_like_bf16((B, sq, Hq, d), x.dtype) if poison else torch.empty((B, sq, Hq, d), dtype=q.dtype, device="cuda")
     lse = G.nan_f32((B, Hq, sq)) if poison else torch.empty((B, Hq, sq), dtype=torch.float32, device="cuda")
     ws = None
     if workspace == "auto":
@@ -41,7 +41,7 @@ def run_decode(aa, x, num_splits=0, workspace="auto", poison=True):
 
 
 def check(aa, x, tag, **kw):
-    O_ref, L_ref = oracle.attention(x.q, x.k, x.v, x.seqlens, True)
+    O_ref, L_ref = oracle.attention(x.q, x.k, x.v, x.seqlens, True, dtype=x.dtype)
     o, lse = run_decode(aa, x, **kw)
     return G.assert_parity(o, lse, O_ref, L_ref, tag)
 
@@ -219,3 +219,18 @@ def test_gqa_equals_mha_with_repeated_kv_heads(aa):
     assert np.abs(l_gqa - l_mha).max() <= 1e-4 * max(1.0, np.abs(l_mha).max())
     O_ref, L_ref = oracle.attention(x.q, x.k, x.v, x.seqlens, True)
     G.assert_parity(o_mha, l_mha, O_ref, L_ref, "mha-repeated")
+
+
+@pytest.mark.parametrize("shape", [
+    # B, Hq, Hkv, d, sq, S, lengths
+    (1, 8, 1, 64, 1, 512, [512]),
+    (4, 32, 8, 128, 1, 3000, [3000, 1, 0, 1777]),
+    (3, 16, 8, 64, 4, 2048, [2048, 900, 5]),
+    (2, 16, 2, 128, 2, 1500, [1500, 64]),
+])
+@pytest.mark.parametrize("num_splits", [0, 1, 5])
+def test_f16_decode_parity(aa, shape, num_splits):
+    """IEEE fp16 decode (attn_decode_f16) against the oracle reading the same fp16 bits; NaN-poisoned cache tail."""
+    B, Hq, Hkv, d, sq, S, lens = shape
+    x = wl.make_decode(B, Hq, Hkv, d, sq, S, lens, seed=301 + d + sq, dtype="f16")
+    check(aa, x, f"f16 {shape} pieces={num_splits}", num_splits=num_splits)

@@ -26,8 +26,8 @@ def aa():
 
 def run_fwd(aa, x, causal=True):
     B, Sq, Hq, d = x.q.shape
-    q, k, v = G.dev_bf16(x.q), G.dev_bf16(x.k), G.dev_bf16(x.v)
-    o = G.nan_like_bf16((B, Sq, Hq, d))
+    q, k, v = G.dev_bf16(x.q, x.dtype), G.dev_bf16(x.k, x.dtype), G.dev_bf16(x.v, x.dtype)
+    o = G.nan_like_bf16((B, Sq, Hq, d), x.dtype)
     lse = G.nan_f32((B, Hq, Sq))
     aa.attn_fwd(q, k, v, o, lse, causal=causal)
     G.torch().cuda.synchronize()
@@ -103,3 +103,32 @@ def test_fwd_gqa_equals_mha_with_repeated_kv_heads(aa):
     o_mha, l_mha = run_fwd(aa, x, True)
     # The same kernel computes both with identical per-column arithmetic.
     assert np.array_equal(o_gqa, o_mha) and np.array_equal(l_gqa, l_mha)
+
+
+@pytest.mark.parametrize("shape", [
+    # B, Sq, Sk, Hq, Hkv, d, causal
+    (1, 200, 200, 4, 4, 128, True),
+    (2, 130, 130, 4, 2, 64, True),
+    (1, 128, 300, 2, 1, 128, True),
+    (1, 300, 128, 2, 2, 128, True),
+    (1, 257, 257, 2, 2, 128, False),
+    (2, 64, 1000, 4, 4, 64, False),
+])
+def test_fwd_f16_small_shapes(aa, shape):
+    """IEEE fp16 inputs and outputs (attn_fwd_f16) against the oracle reading the same fp16 bits."""
+    B, Sq, Sk, Hq, Hkv, d, causal = shape
+    x = wl.make_prefill(B, Hq, Hkv, d, Sq, Sk, seed=181 + Sq + Sk + d, dtype="f16")
+    O_ref, L_ref = oracle.attention(x.q, x.k, x.v, None, causal, dtype="f16")
+    o, lse = run_fwd(aa, x, causal)
+    G.assert_parity(o, lse, O_ref, L_ref, f"fwd f16 {shape}")
+
+
+def test_fwd_page_correctness_config_in_its_dtype(aa):
+    """The FA4 lesson's correctness test as stated: fp16 in, GQA 32/8, S=1024, D=128, rtol = atol = 1e-2."""
+    g = json.load(open(os.path.join(GOLD, "fa4_correctness_config.json")))
+    x = wl.make_prefill(g["batch"], g["n_q_heads"], g["n_kv_heads"], g["head_dim"], g["seqlen"],
+                        g["seqlen"], seed=183, dtype="f16")
+    O_ref, L_ref = oracle.attention(x.q, x.k, x.v, None, True, dtype="f16")
+    o, lse = run_fwd(aa, x, True)
+    assert np.allclose(o, O_ref, rtol=g["rtol"], atol=g["atol"])
+    G.assert_parity(o, lse, O_ref, L_ref, "fa4 correctness config, fp16")
