@@ -35,6 +35,9 @@ namespace attn {
 namespace {
 
 constexpr float kRescaleLog2 = 8.f;  // tolerated growth of the row max (base 2)
+// Fourth word of a raw buffer descriptor: 32-bit data format (a nonzero
+// format is required for the loads to return data), no swizzle, no stride.
+constexpr int kBufferWord3 = 0x00020000;
 
 __device__ __forceinline__ int swap_bits23(int i) {
   return (i & ~12) | ((i >> 1) & 4) | ((i << 1) & 8);
@@ -128,20 +131,29 @@ fwd_pp(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     for (int kk = 0; kk < KST; ++kk) qop[kk] = ok ? ldg16(qp + (2 * kk + hl) * 8) : make_uint4(0, 0, 0, 0);
   }
 
-  // Staging: group A moves K tiles, group B V tiles (rows past Sk are
-  // clamped to Sk - 1: finite data that the mask excludes).
+  // Staging: group A moves K tiles, group B V tiles, through a buffer
+  // descriptor per block whose base is the block's first row and whose size
+  // ends with the sequence's last row. Rows past Sk read as zero (the mask
+  // excludes them), and the only per-lane address is a constant offset: no
+  // vector address arithmetic per load.
   const size_t rstride = (size_t)Hkv * D;
   const uint16_t *src = (G == 0 ? k : v) + ((size_t)b * Sk * Hkv + gk) * D;
+  const long long src_bytes = ((long long)Sk * Hkv - gk) * D * 2;  // src to the end of batch b
   uint16_t *const dtile = G == 0 ? ktile : vtile;
   const int drow = G == 0 ? KROW : VROW, dsize = G == 0 ? KT : VT;
   const int tg = tid & 255, trow = tg / CH, tcol = (tg % CH) * 8;
+  const int voff = (int)((trow * rstride + tcol) * 2);
   uint4 sreg[NKL];
   auto load_blk = [&](int blk) {
+    const long long boff = (long long)blk * BN * (long long)rstride * 2;
+    const long long left = src_bytes - boff;
+    const int nrec = left <= 0 ? 0 : (left > 0x7fffffffLL ? 0x7fffffff : (int)left);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(reinterpret_cast<const char *>(src) + (left <= 0 ? 0 : boff)), (short)0, nrec, kBufferWord3);
 #pragma unroll
-    for (int qi = 0; qi < NKL; ++qi) {
-      const int pr = min(blk * BN + RPT * qi + trow, Sk - 1);
-      sreg[qi] = ldg16(src + (size_t)pr * rstride + tcol);
-    }
+    for (int qi = 0; qi < NKL; ++qi)
+      sreg[qi] = __builtin_bit_cast(
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff + (int)(qi * RPT * rstride * 2), 0, 0));
   };
   auto store_blk = [&](int blk) {
     uint16_t *dst = dtile + (blk & 1) * dsize + trow * drow + tcol;
@@ -257,8 +269,8 @@ fwd_pp(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
       const uint4 a = ring[g % KDEP];
       if constexpr (g + KDEP < 2 * NPV) ring[g % KDEP] = rd(g + KDEP);
       // This group's share of the staging (see stage below), unconditional in
-      // the steady range: blocks past the last are clamped re-reads of the
-      // last rows, written to a slot nobody reads again.
+      // the steady range: a block past the work-group's last is loaded (rows
+      // past Sk as zeros) into a slot nobody reads again.
       if constexpr (g == 2) store_blk(j + 1 - G);
       if constexpr (g == 6) load_blk(j + 2 - G);
       if constexpr (g < NPV) {
