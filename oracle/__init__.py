@@ -1,4 +1,4 @@
-"""CPU oracle for the fused attention forward pass (decode and causal prefill).
+"""CPU oracle for fused attention: forward (decode and causal prefill) and backward.
 
 TEST INFRASTRUCTURE ONLY. Nothing on the product path may import, call or run
 anything in this package: only the test suite, the package smoke check and the
@@ -25,4 +25,5 @@ from .attention import (  # noqa: F401
     combine_partials,
     decode_row_counts,
 )
+from .backward import attention_backward, backward_f64, backward_kv_head  # noqa: F401
 from .brute import brute_attention  # noqa: F401

@@ -26,7 +26,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 CHUNK = 1 << 22
-TID_Q, TID_K, TID_V, TID_LEN = 1, 2, 3, 4
+TID_Q, TID_K, TID_V, TID_LEN, TID_DO = 1, 2, 3, 4, 5
 BF16_NAN = np.uint16(0x7FC0)
 BF16_ZERO = np.uint16(0)
 F16_NAN = np.uint16(0x7E00)
@@ -195,6 +195,11 @@ def make_prefill(batch, n_q_heads, n_kv_heads, d, seqlen_q, seqlen_k, seed,
     v = normal_bits(seed, TID_V, batch * seqlen_k * n_kv_heads * d, dtype=dtype).reshape(
         batch, seqlen_k, n_kv_heads, d)
     return PrefillInputs(q, k, v, dict(seed=seed), dtype)
+
+
+def make_grad_out(q: np.ndarray, seed: int, dtype: str = "bf16") -> np.ndarray:
+    """Output gradient dO shaped like q: N(0,1) draws of stream (seed, TID_DO)."""
+    return normal_bits(seed, TID_DO, q.size, dtype=dtype).reshape(q.shape)
 
 
 def prefill_inputs(cfg: PrefillConfig | str) -> PrefillInputs:
