@@ -1,4 +1,4 @@
-"""Python binding of libattn.so, the gfx950 attention library (decode + prefill).
+"""Python binding of libattn.so, the gfx950 attention library (decode, prefill, backward).
 
 Argument marshalling only: every step of the computation runs in the HIP
 kernels behind the C ABI declared in include/attn.h. The functions here take
@@ -27,7 +27,8 @@ ATTN_MAX_BATCH = 8192
 
 # Every symbol include/attn.h declares.
 EXPORTS = ("attn_decode_plan", "attn_decode_workspace_size", "attn_decode", "attn_decode_ex",
-           "attn_decode_f16", "attn_fwd", "attn_fwd_f16", "attn_status_string", "attn_version")
+           "attn_decode_f16", "attn_fwd", "attn_fwd_f16", "attn_bwd_workspace_size", "attn_bwd",
+           "attn_bwd_f16", "attn_status_string", "attn_version")
 
 _lib = None
 
@@ -60,6 +61,12 @@ def lib() -> ctypes.CDLL:
         getattr(L, name).restype = i32
     for name in ("attn_fwd", "attn_fwd_f16"):
         getattr(L, name).argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp]
+        getattr(L, name).restype = i32
+    L.attn_bwd_workspace_size.argtypes = [i32, i32, i32]
+    L.attn_bwd_workspace_size.restype = sz
+    for name in ("attn_bwd", "attn_bwd_f16"):
+        getattr(L, name).argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, sz,
+                                     vp]
         getattr(L, name).restype = i32
     L.attn_status_string.argtypes = [i32]
     L.attn_status_string.restype = ctypes.c_char_p
@@ -188,3 +195,39 @@ def attn_fwd(q, k, v, o, lse=None, causal=True, stream=None):
             _stream_ptr(stream))
     if st != ATTN_OK:
         raise AttnError(st, "attn_fwd")
+
+
+def attn_bwd_workspace_size(batch, n_q_heads, seqlen_q) -> int:
+    """Bytes of workspace attn_bwd needs (uninitialised memory is fine)."""
+    return int(lib().attn_bwd_workspace_size(batch, n_q_heads, seqlen_q))
+
+
+def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, causal=True, stream=None):
+    """Attention backward. q, o, dout, dq: bf16 or fp16 [B, Sq, Hq, d]; k, v, dk, dv: same
+    type [B, Sk, Hkv, d]; lse: fp32 [B, Hq, Sq] from the forward; workspace: device memory
+    of at least attn_bwd_workspace_size(B, Hq, Sq) bytes."""
+    import torch
+    et, f16 = _elem(q)
+    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout"), (dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _check(t, nm, et, 4)
+    _check(lse, "lse", torch.float32, 3)
+    B, Sq, Hq, d = q.shape
+    _, Sk, Hkv, dk_ = k.shape
+    if tuple(v.shape) != tuple(k.shape) or dk_ != d or k.shape[0] != B:
+        raise ValueError("k and v must be [B, Sk, Hkv, d] matching q")
+    for t, nm in ((o, "o"), (dout, "dout"), (dq, "dq")):
+        if tuple(t.shape) != tuple(q.shape):
+            raise ValueError(f"{nm} must match q")
+    for t, nm in ((dk, "dk"), (dv, "dv")):
+        if tuple(t.shape) != tuple(k.shape):
+            raise ValueError(f"{nm} must match k")
+    if tuple(lse.shape) != (B, Hq, Sq):
+        raise ValueError("lse must be [B, Hq, Sq]")
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous device memory")
+    wbytes = workspace.numel() * workspace.element_size()
+    fn = lib().attn_bwd_f16 if f16 else lib().attn_bwd
+    st = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+            1 if causal else 0, B, Sq, Sk, Hq, Hkv, d, _ptr(workspace), wbytes, _stream_ptr(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_bwd")

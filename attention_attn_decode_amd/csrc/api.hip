@@ -17,6 +17,10 @@ hipError_t launch_decode(const void *q, const void *k, const void *v, const int3
 hipError_t launch_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int causal,
                       int batch, int Sq, int Sk, int Hq, int Hkv, int d, float scale_log2, bool f16,
                       hipStream_t stream);
+hipError_t launch_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse, const void *dout,
+                      void *dq, void *dk, void *dv, int causal, int batch, int Sq, int Sk, int Hq, int Hkv, int d,
+                      float *l2ws, float *dws, bool f16, hipStream_t stream);
+int bwd_sq_pad(int Sq);
 }  // namespace attn
 
 namespace {
@@ -134,9 +138,59 @@ int fwd_impl(const void *q, const void *k, const void *v, void *o, float *lse, i
   return err == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
+// Backward workspace: base-2 LSE and D per (batch, head) row, rows padded to
+// a multiple of 128 queries.
+size_t bwd_workspace(int batch, int n_q_heads, int seqlen_q) {
+  return 2 * (size_t)batch * (size_t)n_q_heads * (size_t)attn::bwd_sq_pad(seqlen_q) * sizeof(float);
+}
+
+int bwd_impl(const void *q, const void *k, const void *v, const void *o, const float *lse, const void *dout,
+             void *dq, void *dk, void *dv, int causal, int batch, int seqlen_q, int seqlen_k, int n_q_heads,
+             int n_kv_heads, int d, void *workspace, size_t workspace_bytes, void *stream, bool f16) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !workspace) return ATTN_ERR_INVALID;
+  if (batch <= 0 || seqlen_q <= 0 || seqlen_k <= 0 || n_q_heads <= 0 || n_kv_heads <= 0)
+    return ATTN_ERR_INVALID;
+  if (n_q_heads % n_kv_heads != 0) return ATTN_ERR_INVALID;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  if (n_q_heads > 65535) return ATTN_ERR_UNSUPPORTED;  // keeps in-tile byte offsets in 32 bits
+  const long long qtiles = (long long)(seqlen_q + 127) / 128 * batch * n_q_heads;
+  const long long ktiles = (long long)(seqlen_k + 127) / 128 * batch * n_kv_heads;
+  const long long rows = (long long)attn::bwd_sq_pad(seqlen_q) * batch * n_q_heads;
+  if (qtiles > 0x7fffffffLL || ktiles > 0x7fffffffLL || rows > 0x3fffffffLL) return ATTN_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(dq) ||
+      !aligned16(dk) || !aligned16(dv) || !aligned4(lse) || !aligned16(workspace))
+    return ATTN_ERR_MISALIGNED;
+  if (workspace_bytes < bwd_workspace(batch, n_q_heads, seqlen_q)) return ATTN_ERR_WORKSPACE;
+  float *l2ws = static_cast<float *>(workspace);
+  float *dws = l2ws + rows;
+  const hipError_t err =
+      attn::launch_bwd(q, k, v, o, lse, dout, dq, dk, dv, causal ? 1 : 0, batch, seqlen_q, seqlen_k, n_q_heads,
+                       n_kv_heads, d, l2ws, dws, f16, static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t attn_bwd_workspace_size(int batch, int n_q_heads, int seqlen_q) {
+  if (batch <= 0 || n_q_heads <= 0 || seqlen_q <= 0) return 0;
+  return bwd_workspace(batch, n_q_heads, seqlen_q);
+}
+
+int attn_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse, const void *dout,
+             void *dq, void *dk, void *dv, int causal, int batch, int seqlen_q, int seqlen_k, int n_q_heads,
+             int n_kv_heads, int d, void *workspace, size_t workspace_bytes, void *stream) {
+  return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, causal, batch, seqlen_q, seqlen_k, n_q_heads, n_kv_heads, d,
+                  workspace, workspace_bytes, stream, false);
+}
+
+int attn_bwd_f16(const void *q, const void *k, const void *v, const void *o, const float *lse, const void *dout,
+                 void *dq, void *dk, void *dv, int causal, int batch, int seqlen_q, int seqlen_k, int n_q_heads,
+                 int n_kv_heads, int d, void *workspace, size_t workspace_bytes, void *stream) {
+  return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, causal, batch, seqlen_q, seqlen_k, n_q_heads, n_kv_heads, d,
+                  workspace, workspace_bytes, stream, true);
+}
 
 int attn_decode_ex(const void *q, const void *k_cache, const void *v_cache,
                    const int32_t *seqlens_k, void *o, float *lse, int n_q_heads, int n_kv_heads,

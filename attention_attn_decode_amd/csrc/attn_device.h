@@ -131,17 +131,21 @@ __device__ __forceinline__ int chunk_swz(int r) {
 
 __device__ __forceinline__ uint4 ldg16(const uint16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
 __device__ __forceinline__ uint4 lds16(const uint16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
-// A 16-byte LDS operand fetched as two 8-byte reads: on gfx950 ds_read_b64
-// sustains about twice the bytes per clock of ds_read_b128. The accesses are
-// volatile only so that the compiler does not merge them back into one
-// 16-byte read.
-__device__ __forceinline__ uint4 lds16_as_2x8(const uint16_t *p) {
-  typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
-  typedef const volatile u32x2 __attribute__((address_space(3))) *lds_ptr;
-  const u32x2 a = *(lds_ptr)(reinterpret_cast<uintptr_t>(p));
-  const u32x2 b = *(lds_ptr)(reinterpret_cast<uintptr_t>(p + 4));
-  return make_uint4(a[0], a[1], b[0], b[1]);
-}
 __device__ __forceinline__ void sts16(uint16_t *p, const uint4 &v) { *reinterpret_cast<uint4 *>(p) = v; }
+
+// Fourth word of a raw buffer descriptor: 32-bit data format (a nonzero
+// format is required for the loads to return data), no swizzle, no stride.
+constexpr int kBufferWord3 = 0x00020000;
+
+// Raw buffer descriptor over [base, base + bytes): loads at offsets past the
+// end return zero. bytes <= 0 gives an empty range; sizes above 2^31 - 1 are
+// clamped (every caller's offsets stay below that).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, long long bytes) {
+  const int n = bytes <= 0 ? 0 : (bytes > 0x7fffffffLL ? 0x7fffffff : (int)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, kBufferWord3);
+}
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t rs, int byte_off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, byte_off, 0, 0));
+}
 
 }  // namespace attn

@@ -1,0 +1,468 @@
+// Attention backward for gfx950: dQ, dK, dV from Q, K, V, O, LSE and dO.
+//
+// Pages cited by title and section:
+//   [FA4-bwd]   "Optimization diaries: Improving FlashAttention-4 backward pass
+//                kernel design for head dimension 64"
+//   [FA4-edges] "Flash Attention 4 — warp-role choreography and the edges"
+//
+// With s = 1/sqrt(d) and L the natural-log LSE of the forward
+// ([FA4-bwd] §Recap on the FA4 backward pass):
+//   P = exp(s Q K^T - L),  dP = dO V^T,  dS = P o (dP - D),
+//   dV = P^T dO,  dK = s dS^T Q,  dQ = s dS K,  D = rowsum(dO o O).
+//
+// Three kernels, no atomics and no zero-initialised memory:
+//   bwd_pre   D and L * log2(e) per query row, into the caller's workspace.
+//   bwd_dkdv  one work-group per (batch, KV head, 128-key tile), as in the
+//             page's recap: it owns its K and V rows, walks the query tiles
+//             of every query head that reads its KV head (GQA heads summed in
+//             registers) and writes dK and dV once.
+//   bwd_dq    one work-group per (batch, query head, 128-row tile): it owns its
+//             Q and dO rows, walks the key tiles and writes dQ once.
+// The page sums dQ contributions from the KV-tile owners into an fp32 buffer
+// in global memory. Here dQ has its own pass that recomputes S and dP (seven
+// products per (query, key) tile instead of five): no atomic traffic (which
+// would be about Sk / 128 times the size of dQ), no zeroed accumulator, and
+// bitwise-reproducible results.
+//
+// Both main kernels use the forward's swap-AB orientation for the tile they
+// own: the owned rows (keys in bwd_dkdv, queries in bwd_dq) are the MFMA N
+// dimension held in registers, one row per lane, and the streamed tile is
+// the LDS operand. Every product is a v_mfma_f32_32x32x16 and every
+// probability tile feeds the next product straight from registers: the
+// accumulator of a 32 x 32 tile is, lane for lane, the B operand of a product
+// contracting over its rows, once the rows are read in the order pi (bits 2
+// and 3 of the row index swapped). The streamed tiles are read both row-wise
+// (products contracting over d) and transposed (products contracting over
+// rows, ds_read_b64_tr_b16); an XOR swizzle of their 16-byte chunks keeps both
+// read patterns free of bank conflicts.
+//
+// Masking ([FA4-edges] §Edge 1 · causal masking) is bottom-right aligned as in
+// the forward: query i sees keys j <= i + Sk - Sq. Masked pairs, rows past Sq
+// and keys past Sk get P = dS = 0 by selection, so no infinity or NaN from
+// padding reaches a product.
+#include "attn_device.h"
+
+namespace attn {
+namespace {
+
+constexpr float kLog2e = 1.44269504088896340736f;
+
+__device__ __forceinline__ int pi_row(int i) { return (i & ~12) | ((i >> 1) & 4) | ((i << 1) & 8); }
+
+// Row-major tile of R rows x D elements in LDS, 16-byte chunks XOR-swizzled
+// per row (chunk_swz): element (r, c) lives at r * D + 8 * ((c / 8) ^ swz(r)) + c % 8.
+template <int D>
+__device__ __forceinline__ int tile_off(int r, int chunk) {
+  return r * D + 8 * (chunk ^ chunk_swz<D>(r));
+}
+
+// A operand of a product contracting over the tile's rows: lane (m, h) of
+// 16-row step ks, M-tile mt gets rows 16 ks + 8 h .. +7 of column 32 mt + m,
+// assembled from two transposing reads (rows +0..3 and +4..7).
+template <int D>
+__device__ __forceinline__ uint4 tile_tr_operand(const uint16_t *tile, int lane, int ks, int mt) {
+  const int k = lane & 15, half = (lane >> 4) & 1, hl = lane >> 5;
+  const int c = 4 * mt + 2 * half + ((k & 3) >> 1);
+  const int r0 = 16 * ks + 8 * hl + (k >> 2);
+  const uint2 a = lds_tr4(tile + tile_off<D>(r0, c) + 4 * (k & 1));
+  const uint2 b = lds_tr4(tile + tile_off<D>(r0 + 4, c) + 4 * (k & 1));
+  return make_uint4(a.x, a.y, b.x, b.y);
+}
+
+// A operand of a product contracting over d: lane (n, h) of 32-row tile t,
+// k-step kk gets row 32 t + pi(n), elements 16 kk + 8 h .. +7.
+template <int D>
+__device__ __forceinline__ uint4 tile_row_operand(const uint16_t *tile, int lane, int t, int kk) {
+  const int r = 32 * t + pi_row(lane & 31);
+  return lds16(tile + tile_off<D>(r, 2 * kk + (lane >> 5)));
+}
+
+// ---------------------------------------------------------------------------
+// D = rowsum(dO o O) and L2 = L * log2(e) (+inf for a row that sees no key)
+// per (batch, head, query) row, rows padded to Sq_pad with D = 0, L2 = +inf.
+template <int D>
+__global__ void __launch_bounds__(256)
+bwd_pre(const uint16_t *__restrict__ o, const uint16_t *__restrict__ dout, const float *__restrict__ lse,
+        float *__restrict__ l2ws, float *__restrict__ dws, int B, int Sq, int Sq_pad, int Hq, bool f16) {
+  constexpr int LPR = D / 8;  // lanes per row
+  const int rows_per_block = 256 / LPR;
+  const long long total = (long long)B * Hq * Sq_pad;
+  const int sub = threadIdx.x % LPR;
+  for (long long row = (long long)blockIdx.x * rows_per_block + threadIdx.x / LPR; row < total;
+       row += (long long)gridDim.x * rows_per_block) {
+    const int i = (int)(row % Sq_pad);
+    const long long bh = row / Sq_pad;
+    const int h = (int)(bh % Hq), b = (int)(bh / Hq);
+    float acc = 0.f, l2 = __builtin_inff();
+    if (i < Sq) {
+      const size_t off = ((size_t)((size_t)b * Sq + i) * Hq + h) * D + 8 * sub;
+      const uint4 ov = ldg16(o + off), gv = ldg16(dout + off);
+      const uint32_t ow[4] = {ov.x, ov.y, ov.z, ov.w}, gw[4] = {gv.x, gv.y, gv.z, gv.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float o0, o1, g0, g1;
+        if (f16) {
+          const f16x2 a = __builtin_bit_cast(f16x2, ow[e]), c = __builtin_bit_cast(f16x2, gw[e]);
+          o0 = (float)a[0], o1 = (float)a[1], g0 = (float)c[0], g1 = (float)c[1];
+        } else {
+          o0 = __uint_as_float(ow[e] << 16), o1 = __uint_as_float(ow[e] & 0xffff0000u);
+          g0 = __uint_as_float(gw[e] << 16), g1 = __uint_as_float(gw[e] & 0xffff0000u);
+        }
+        acc = __builtin_fmaf(o0, g0, acc);
+        acc = __builtin_fmaf(o1, g1, acc);
+      }
+      const float L = lse[(size_t)bh * Sq + i];
+      l2 = L == kNegInf ? __builtin_inff() : L * kLog2e;
+    }
+#pragma unroll
+    for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, LPR);
+    if (sub == 0) {
+      dws[row] = i < Sq ? acc : 0.f;
+      l2ws[row] = l2;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV. Work-group = 4 waves x 32 keys = one 128-key tile of (b, KV head g);
+// query tiles of 32 rows of each of the G query heads of g pass through LDS.
+constexpr int kKT = 128;  // keys per dK/dV work-group
+constexpr int kQB = 32;   // query rows per dK/dV step
+
+template <int D, bool F16>
+__global__ void __launch_bounds__(256, D == 128 ? 1 : 2)
+bwd_dkdv(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+         const uint16_t *__restrict__ dout, const float *__restrict__ l2ws, const float *__restrict__ dws,
+         uint16_t *__restrict__ dk, uint16_t *__restrict__ dv, int Sq, int Sq_pad, int Sk, int Hq, int Hkv,
+         int causal, float scale_log2, float scale, int BHkv) {
+  constexpr int KST = D / 16, MT = D / 32, CH = D / 8;
+  constexpr int QT = kQB * D;                 // one Q (or dO) tile, elements
+  constexpr int LPT = kQB * CH / 256;         // 16-byte chunks per thread per tile
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * QT];  // {Q, dO} x 2 slots
+
+  const int x = blockIdx.x;
+  const int kt = x / BHkv;  // key tile 0 first: under a causal mask it has the most queries
+  const int u = x % BHkv;
+  const int b = u / Hkv, g = u % Hkv;
+  const int G = Hq / Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 31, hl = lane >> 5;
+  const int k0 = kt * kKT, kw0 = k0 + 32 * w;  // first key of the tile, of the wave
+  const int key = kw0 + n;
+  const int off = Sk - Sq;
+
+  // This lane's K and V row as B operands (d contracted), zero past Sk.
+  uint4 kop[KST], vop[KST];
+  {
+    const size_t roff = ((size_t)((size_t)b * Sk + (key < Sk ? key : 0)) * Hkv + g) * D;
+#pragma unroll
+    for (int kk = 0; kk < KST; ++kk) {
+      const bool ok = key < Sk;
+      kop[kk] = ok ? ldg16(k + roff + (2 * kk + hl) * 8) : make_uint4(0, 0, 0, 0);
+      vop[kk] = ok ? ldg16(v + roff + (2 * kk + hl) * 8) : make_uint4(0, 0, 0, 0);
+    }
+  }
+  f32x16 dkT[MT], dvT[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dkT[mt][r] = 0.f, dvT[mt][r] = 0.f;
+
+  // Query rows that can see a key of this tile: i >= k0 - off (all if not causal).
+  const int i_first = causal ? max(0, k0 - off) : 0;
+  const int ib0 = i_first / kQB, nqb = (Sq + kQB - 1) / kQB;
+  const int nsteps = ib0 < nqb ? (nqb - ib0) * G : 0;
+  const int wave_first_i = causal ? kw0 - off : -0x40000000;  // first query that sees the wave's first key
+
+  const size_t rstride = (size_t)Hq * D;
+  const int tg = tid, trow = tg / CH, tch = tg % CH;
+  uint4 sq[LPT], sdo[LPT];
+  auto load_step = [&](int st) {
+    const int hh = st / (nqb - ib0), ib = ib0 + st % (nqb - ib0);
+    const int h = g * G + hh;
+    const long long base = ((long long)b * Sq * Hq + h) * D + (long long)ib * kQB * rstride;
+    const long long left = ((long long)Sq * Hq - h) * D * 2 - (long long)ib * kQB * rstride * 2;
+    const auto rq = buffer_rsrc(q + base, left), rd = buffer_rsrc(dout + base, left);
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const int boff = (int)(((trow + i * (256 / CH)) * rstride + tch * 8) * 2);
+      sq[i] = buf_load16(rq, boff);
+      sdo[i] = buf_load16(rd, boff);
+    }
+  };
+  auto store_step = [&](int slot) {
+    uint16_t *qt = smem + slot * 2 * QT, *dt = qt + QT;
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const int r = trow + i * (256 / CH);
+      sts16(qt + tile_off<D>(r, tch), sq[i]);
+      sts16(dt + tile_off<D>(r, tch), sdo[i]);
+    }
+  };
+
+  if (nsteps > 0) {
+    load_step(0);
+    store_step(0);
+  }
+  __syncthreads();
+  for (int st = 0; st < nsteps; ++st) {
+    if (st + 1 < nsteps) load_step(st + 1);
+    const int hh = st / (nqb - ib0), ib = ib0 + st % (nqb - ib0);
+    const int h = g * G + hh;
+    const int i0 = ib * kQB;
+    const uint16_t *qt = smem + (st & 1) * 2 * QT, *dt = qt + QT;
+    // Skip when every query of the step is before the wave's first visible one.
+    if (i0 + kQB - 1 >= wave_first_i && kw0 < Sk) {
+      f32x16 S, dP;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) S[r] = 0.f, dP[r] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < KST; ++kk) {
+        S = mma32<F16>(tile_row_operand<D>(qt, lane, 0, kk), kop[kk], S);
+        dP = mma32<F16>(tile_row_operand<D>(dt, lane, 0, kk), vop[kk], dP);
+      }
+      // Register r holds query i0 + 16 (r / 8) + 8 hl + r % 8.
+      const float *l2p = l2ws + ((size_t)b * Hq + h) * Sq_pad + i0 + 8 * hl;
+      const float *dp = dws + ((size_t)b * Hq + h) * Sq_pad + i0 + 8 * hl;
+      float l2v[16], dv_[16];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int qd = 0; qd < 2; ++qd) {
+          const float4 a = *reinterpret_cast<const float4 *>(l2p + 16 * hf + 4 * qd);
+          const float4 c = *reinterpret_cast<const float4 *>(dp + 16 * hf + 4 * qd);
+          l2v[8 * hf + 4 * qd + 0] = a.x, l2v[8 * hf + 4 * qd + 1] = a.y;
+          l2v[8 * hf + 4 * qd + 2] = a.z, l2v[8 * hf + 4 * qd + 3] = a.w;
+          dv_[8 * hf + 4 * qd + 0] = c.x, dv_[8 * hf + 4 * qd + 1] = c.y;
+          dv_[8 * hf + 4 * qd + 2] = c.z, dv_[8 * hf + 4 * qd + 3] = c.w;
+        }
+      const int lim = causal ? key - off : -0x40000000;  // query i sees this key iff i >= lim
+      uint4 pP[2], pS[2];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        float pv[8], sv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int r = 8 * hf + e;
+          const int qi = i0 + 16 * hf + 8 * hl + e;
+          const bool vis = key < Sk && qi < Sq && qi >= lim;
+          const float p = vis ? exp2_hw(__builtin_fmaf(S[r], scale_log2, -l2v[r])) : 0.f;
+          pv[e] = p;
+          sv[e] = vis ? p * (dP[r] - dv_[r]) : 0.f;
+        }
+        pP[hf] = make_uint4(pack2<F16>(pv[0], pv[1]), pack2<F16>(pv[2], pv[3]), pack2<F16>(pv[4], pv[5]),
+                            pack2<F16>(pv[6], pv[7]));
+        pS[hf] = make_uint4(pack2<F16>(sv[0], sv[1]), pack2<F16>(sv[2], sv[3]), pack2<F16>(sv[4], sv[5]),
+                            pack2<F16>(sv[6], sv[7]));
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          dvT[mt] = mma32<F16>(tile_tr_operand<D>(dt, lane, ks, mt), pP[ks], dvT[mt]);
+          dkT[mt] = mma32<F16>(tile_tr_operand<D>(qt, lane, ks, mt), pS[ks], dkT[mt]);
+        }
+    }
+    if (st + 1 < nsteps) store_step((st + 1) & 1);
+    __syncthreads();
+  }
+
+  if (key >= Sk) return;
+  const size_t ooff = ((size_t)((size_t)b * Sk + key) * Hkv + g) * D;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int dd = 32 * mt + 8 * a + 4 * hl;
+      *reinterpret_cast<uint2 *>(dk + ooff + dd) =
+          make_uint2(pack2<F16>(dkT[mt][4 * a] * scale, dkT[mt][4 * a + 1] * scale),
+                     pack2<F16>(dkT[mt][4 * a + 2] * scale, dkT[mt][4 * a + 3] * scale));
+      *reinterpret_cast<uint2 *>(dv + ooff + dd) =
+          make_uint2(pack2<F16>(dvT[mt][4 * a], dvT[mt][4 * a + 1]), pack2<F16>(dvT[mt][4 * a + 2], dvT[mt][4 * a + 3]));
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dQ. Work-group = 4 waves x 32 query rows = one 128-row tile of (b, head h);
+// 64-key K and V tiles pass through LDS.
+constexpr int kQT = 128;  // query rows per dQ work-group
+constexpr int kKB = 64;   // keys per dQ step
+
+template <int D, bool F16>
+__global__ void __launch_bounds__(256, D == 128 ? 1 : 2)
+bwd_dq(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+       const uint16_t *__restrict__ dout, const float *__restrict__ l2ws, const float *__restrict__ dws,
+       uint16_t *__restrict__ dq, int Sq, int Sq_pad, int Sk, int Hq, int Hkv, int causal, float scale_log2,
+       float scale, int n_qtiles, int BH) {
+  constexpr int KST = D / 16, MT = D / 32, CH = D / 8;
+  constexpr int KTL = kKB * D;          // one K (or V) tile, elements
+  constexpr int LPT = kKB * CH / 256;   // 16-byte chunks per thread per tile
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * KTL];  // {K, V} x 2 slots
+
+  const int x = blockIdx.x;
+  const int qt_ = n_qtiles - 1 - x / BH;  // last query tile first: the longest key range under a causal mask
+  const int u = x % BH;
+  const int b = u / Hq, h = u % Hq;
+  const int gk = h / (Hq / Hkv);
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 31, hl = lane >> 5;
+  const int q0 = qt_ * kQT, r0 = q0 + 32 * w;
+  const int qrow = r0 + n;
+  const int off = Sk - Sq;
+
+  uint4 qop[KST], doop[KST];
+  {
+    const bool ok = qrow < Sq;
+    const size_t roff = ((size_t)((size_t)b * Sq + (ok ? qrow : 0)) * Hq + h) * D;
+#pragma unroll
+    for (int kk = 0; kk < KST; ++kk) {
+      qop[kk] = ok ? ldg16(q + roff + (2 * kk + hl) * 8) : make_uint4(0, 0, 0, 0);
+      doop[kk] = ok ? ldg16(dout + roff + (2 * kk + hl) * 8) : make_uint4(0, 0, 0, 0);
+    }
+  }
+  const float l2 = l2ws[((size_t)b * Hq + h) * Sq_pad + qrow];  // qrow < Sq_pad: padded rows hold +inf
+  const float Dr = dws[((size_t)b * Hq + h) * Sq_pad + qrow];
+  f32x16 dqT[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dqT[mt][r] = 0.f;
+
+  int kend = causal ? min(Sk, q0 + kQT + off) : Sk;  // keys any row of the tile sees
+  if (kend < 0) kend = 0;
+  const int nblk = (kend + kKB - 1) / kKB;
+  // Keys a row of this wave can see: j <= r0 + 31 + off.
+  const int wave_kend = causal ? min(Sk, r0 + 32 + off) : Sk;
+  const int lim = causal ? qrow + off : 0x3fffffff;  // this row sees keys j <= lim
+
+  const size_t rstride = (size_t)Hkv * D;
+  const int trow = tid / CH, tch = tid % CH;
+  uint4 sk[LPT], sv[LPT];
+  auto load_blk = [&](int blk) {
+    const long long base = ((long long)b * Sk * Hkv + gk) * D + (long long)blk * kKB * rstride;
+    const long long left = ((long long)Sk * Hkv - gk) * D * 2 - (long long)blk * kKB * rstride * 2;
+    const auto rk = buffer_rsrc(k + base, left), rv = buffer_rsrc(v + base, left);
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const int boff = (int)(((trow + i * (256 / CH)) * rstride + tch * 8) * 2);
+      sk[i] = buf_load16(rk, boff);
+      sv[i] = buf_load16(rv, boff);
+    }
+  };
+  auto store_blk = [&](int slot) {
+    uint16_t *ktl = smem + slot * 2 * KTL, *vtl = ktl + KTL;
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const int r = trow + i * (256 / CH);
+      sts16(ktl + tile_off<D>(r, tch), sk[i]);
+      sts16(vtl + tile_off<D>(r, tch), sv[i]);
+    }
+  };
+
+  if (nblk > 0) {
+    load_blk(0);
+    store_blk(0);
+  }
+  __syncthreads();
+  for (int j = 0; j < nblk; ++j) {
+    if (j + 1 < nblk) load_blk(j + 1);
+    const int j0 = j * kKB;
+    const uint16_t *ktl = smem + (j & 1) * 2 * KTL, *vtl = ktl + KTL;
+    if (j0 < wave_kend) {
+      f32x16 S[2], dP[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) S[t][r] = 0.f, dP[t][r] = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < KST; ++kk) {
+          S[t] = mma32<F16>(tile_row_operand<D>(ktl, lane, t, kk), qop[kk], S[t]);
+          dP[t] = mma32<F16>(tile_row_operand<D>(vtl, lane, t, kk), doop[kk], dP[t]);
+        }
+      }
+      // Register r of tile t holds key j0 + 32 t + 16 (r / 8) + 8 hl + r % 8.
+      uint4 pS[4];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          float sv8[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int r = 8 * hf + e;
+            const int kj = j0 + 32 * t + 16 * hf + 8 * hl + e;
+            const bool vis = kj < Sk && kj <= lim && qrow < Sq;
+            const float p = vis ? exp2_hw(__builtin_fmaf(S[t][r], scale_log2, -l2)) : 0.f;
+            sv8[e] = vis ? p * (dP[t][r] - Dr) : 0.f;
+          }
+          pS[2 * t + hf] = make_uint4(pack2<F16>(sv8[0], sv8[1]), pack2<F16>(sv8[2], sv8[3]),
+                                      pack2<F16>(sv8[4], sv8[5]), pack2<F16>(sv8[6], sv8[7]));
+        }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) dqT[mt] = mma32<F16>(tile_tr_operand<D>(ktl, lane, ks, mt), pS[ks], dqT[mt]);
+    }
+    if (j + 1 < nblk) store_blk((j + 1) & 1);
+    __syncthreads();
+  }
+
+  if (qrow >= Sq) return;
+  uint16_t *dst = dq + ((size_t)((size_t)b * Sq + qrow) * Hq + h) * D;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int dd = 32 * mt + 8 * a + 4 * hl;
+      *reinterpret_cast<uint2 *>(dst + dd) =
+          make_uint2(pack2<F16>(dqT[mt][4 * a] * scale, dqT[mt][4 * a + 1] * scale),
+                     pack2<F16>(dqT[mt][4 * a + 2] * scale, dqT[mt][4 * a + 3] * scale));
+    }
+}
+
+}  // namespace
+
+int bwd_sq_pad(int Sq) { return (Sq + kQT - 1) / kQT * kQT; }
+
+hipError_t launch_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse, const void *dout,
+                      void *dq, void *dk, void *dv, int causal, int batch, int Sq, int Sk, int Hq, int Hkv, int d,
+                      float *l2ws, float *dws, bool f16, hipStream_t stream) {
+  const auto *qq = static_cast<const uint16_t *>(q);
+  const auto *kk = static_cast<const uint16_t *>(k);
+  const auto *vv = static_cast<const uint16_t *>(v);
+  const auto *oo = static_cast<const uint16_t *>(o);
+  const auto *gg = static_cast<const uint16_t *>(dout);
+  const int Sq_pad = bwd_sq_pad(Sq);
+  const float scale = 1.f / sqrtf((float)d), scale_log2 = scale * kLog2e;
+  {
+    const long long rows = (long long)batch * Hq * Sq_pad;
+    const int rows_per_block = 256 / (d / 8);
+    const long long blocks = (rows + rows_per_block - 1) / rows_per_block;
+    const dim3 grid((unsigned)(blocks < 65536 ? blocks : 65536));
+    if (d == 128)
+      hipLaunchKernelGGL(bwd_pre<128>, grid, dim3(256), 0, stream, oo, gg, lse, l2ws, dws, batch, Sq, Sq_pad, Hq, f16);
+    else
+      hipLaunchKernelGGL(bwd_pre<64>, grid, dim3(256), 0, stream, oo, gg, lse, l2ws, dws, batch, Sq, Sq_pad, Hq, f16);
+  }
+  const int BHkv = batch * Hkv, BH = batch * Hq;
+  const int n_ktiles = (Sk + kKT - 1) / kKT, n_qtiles = (Sq + kQT - 1) / kQT;
+  auto dkdv = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3(n_ktiles * BHkv), dim3(256), 0, stream, qq, kk, vv, gg, l2ws, dws,
+                       static_cast<uint16_t *>(dk), static_cast<uint16_t *>(dv), Sq, Sq_pad, Sk, Hq, Hkv, causal,
+                       scale_log2, scale, BHkv);
+  };
+  auto dqk = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3(n_qtiles * BH), dim3(256), 0, stream, qq, kk, vv, gg, l2ws, dws,
+                       static_cast<uint16_t *>(dq), Sq, Sq_pad, Sk, Hq, Hkv, causal, scale_log2, scale, n_qtiles, BH);
+  };
+  if (d == 128) {
+    if (f16) dkdv(bwd_dkdv<128, true>), dqk(bwd_dq<128, true>);
+    else dkdv(bwd_dkdv<128, false>), dqk(bwd_dq<128, false>);
+  } else {
+    if (f16) dkdv(bwd_dkdv<64, true>), dqk(bwd_dq<64, true>);
+    else dkdv(bwd_dkdv<64, false>), dqk(bwd_dq<64, false>);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace attn

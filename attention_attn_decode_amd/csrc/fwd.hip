@@ -35,9 +35,6 @@ namespace attn {
 namespace {
 
 constexpr float kRescaleLog2 = 8.f;  // tolerated growth of the row max (base 2)
-// Fourth word of a raw buffer descriptor: 32-bit data format (a nonzero
-// format is required for the loads to return data), no swizzle, no stride.
-constexpr int kBufferWord3 = 0x00020000;
 
 __device__ __forceinline__ int swap_bits23(int i) {
   return (i & ~12) | ((i >> 1) & 4) | ((i << 1) & 8);

@@ -1,6 +1,7 @@
 /*
- * attn.h - fused attention forward for MI355X (gfx950): KV-cache decode with
- * grouped-query attention and split-KV, and (causal) prefill.
+ * attn.h - fused attention for MI355X (gfx950): KV-cache decode with
+ * grouped-query attention and split-KV, (causal) prefill, and the backward
+ * pass of prefill attention.
  *
  * Pages cited by title and section:
  *   [FA4-decode]  "Optimization diaries: S/P ping-pong for FlashAttention-4 decode"
@@ -173,6 +174,43 @@ int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, i
 int attn_fwd_f16(const void *q, const void *k, const void *v, void *o, float *lse, int causal,
                  int batch, int seqlen_q, int seqlen_k, int n_q_heads, int n_kv_heads, int d,
                  void *stream);
+
+/*
+ * Bytes of workspace attn_bwd needs: 2 * batch * n_q_heads * Sq_pad * 4 with
+ * Sq_pad = seqlen_q rounded up to a multiple of 128 (a base-2 LSE and the row
+ * sum D per query row). No initialisation is needed. Returns 0 for invalid
+ * arguments. Host-only.
+ */
+size_t attn_bwd_workspace_size(int batch, int n_q_heads, int seqlen_q);
+
+/*
+ * Attention backward ([FA4-bwd] §Recap on the FA4 backward pass): with
+ * s = 1/sqrt(d), L = lse and D = rowsum(dO o O) (the row sum of P o dP),
+ *   P = exp(s Q K^T - L), dP = dO V^T, dS = P o (dP - D),
+ *   dV = P^T dO, dK = s dS^T Q, dQ = s dS K.
+ *   q, o, dout, dq  [batch][seqlen_q][n_q_heads][d] bf16
+ *   k, v, dk, dv    [batch][seqlen_k][n_kv_heads][d] bf16
+ *   lse             [batch][n_q_heads][seqlen_q] fp32, the forward's natural-log
+ *                   LSE (-inf for a row that sees no key); required.
+ * dq, dk and dv are overwritten (written exactly once each, no accumulation
+ * into the caller's memory). GQA: dk and dv of a KV head sum the G query
+ * heads that read it. causal != 0 applies the forward's bottom-right mask.
+ * Requires d == 64 or d == 128 and a workspace of attn_bwd_workspace_size()
+ * bytes (16-byte aligned). Device work: one row-statistics kernel, then a
+ * kernel per 128-key tile of each (batch, KV head) for dK and dV and a kernel
+ * per 128-row query tile of each (batch, query head) for dQ. No atomics: the
+ * results are deterministic and bitwise reproducible.
+ */
+int attn_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
+             const void *dout, void *dq, void *dk, void *dv, int causal, int batch, int seqlen_q,
+             int seqlen_k, int n_q_heads, int n_kv_heads, int d, void *workspace,
+             size_t workspace_bytes, void *stream);
+
+/* attn_bwd for IEEE fp16 q, k, v, o, dout, dq, dk and dv (same layouts, workspace and errors). */
+int attn_bwd_f16(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                 const void *dout, void *dq, void *dk, void *dv, int causal, int batch, int seqlen_q,
+                 int seqlen_k, int n_q_heads, int n_kv_heads, int d, void *workspace,
+                 size_t workspace_bytes, void *stream);
 
 /* Static description of a status code; never NULL. */
 const char *attn_status_string(int status);

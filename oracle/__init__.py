@@ -25,5 +25,5 @@ from .attention import (  # noqa: F401
     combine_partials,
     decode_row_counts,
 )
-from .backward import attention_backward, backward_f64, backward_kv_head  # noqa: F401
+from .backward import attention_backward, backward_error_scales, backward_f64, backward_kv_head  # noqa: F401
 from .brute import brute_attention  # noqa: F401

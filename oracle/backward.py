@@ -109,3 +109,39 @@ def backward_kv_head(q, k, v, do, b, g, causal=True, dtype="bf16", row_block=512
                                  to_f64(v[b:b + 1, :, g:g + 1], dtype), to_f64(do[b:b + 1, :, sl], dtype),
                                  causal, row_block)
     return dq[0], dk[0, :, 0], dv[0, :, 0], D[0]
+
+
+def backward_error_scales(q, k, v, do, causal=True, dtype="bf16", row_block=512):
+    """Sums of absolute values of the terms of each gradient element.
+
+    A product rounded to a precision with unit roundoff u (relative error at
+    most u per term) errs by at most u times the sum of its terms' absolute
+    values. Returns (eq [B, Sq, Hq, d], ek [B, Sk, Hkv, d], ev [B, Sk, Hkv, d]):
+        ev = P^T |dO|,   ek = s A^T |Q|,   eq = s A |K|,
+    with A = |dS| + 2 P o delta and delta_i = sum_d |dO_i| (P |V|)_i, the scale
+    by which an error of O (itself bounded by u (P |V|)) moves D = rowsum(dO o O).
+    """
+    qf, kf, vf, dof = (to_f64(t, dtype) for t in (q, k, v, do))
+    B, Sq, Hq, d = qf.shape
+    Sk, Hkv = kf.shape[1], kf.shape[2]
+    G = Hq // Hkv
+    scale = 1.0 / math.sqrt(d)
+    eq = np.zeros((B, Sq, Hq, d))
+    ek = np.zeros((B, Sk, Hkv, d))
+    ev = np.zeros((B, Sk, Hkv, d))
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            kk, vv = kf[b, :, g], vf[b, :, g]
+            for i0 in range(0, Sq, row_block):
+                i1 = min(Sq, i0 + row_block)
+                qq, dd = qf[b, i0:i1, h], dof[b, i0:i1, h]
+                p = _probs(qq, kk, _mask(Sq, Sk, causal, i0, i1), scale)
+                dp = dd @ vv.T
+                ds = p * (dp - np.sum(p * dp, axis=1)[:, None])
+                delta = np.sum(np.abs(dd) * (p @ np.abs(vv)), axis=1)
+                a = np.abs(ds) + 2.0 * p * delta[:, None]
+                ev[b, :, g] += p.T @ np.abs(dd)
+                ek[b, :, g] += scale * (a.T @ np.abs(qq))
+                eq[b, i0:i1, h] = scale * (a @ np.abs(kk))
+    return eq, ek, ev

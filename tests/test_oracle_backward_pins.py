@@ -149,3 +149,17 @@ def test_backward_bits_wrappers_agree():
     ref = oracle.backward_f64(*(oracle.f16_bits_to_f64(t) for t in (xf.q, xf.k, xf.v, dof)), False)
     for a, r in zip(got, ref):
         assert np.array_equal(a, r)
+
+
+def test_backward_error_scales_bound_the_gradients():
+    """|dX| <= the sum of its terms' absolute values (triangle inequality), for every element."""
+    x = wl.make_prefill(2, 4, 2, 16, 33, 41, seed=71)
+    do = wl.make_grad_out(x.q, 72)
+    for causal in (True, False):
+        dq, dk, dv, _ = oracle.attention_backward(x.q, x.k, x.v, do, causal)
+        eq, ek, ev = oracle.backward_error_scales(x.q, x.k, x.v, do, causal)
+        assert np.all(np.abs(dv) <= ev + 1e-12)
+        assert np.all(np.abs(dk) <= ek + 1e-12)
+        assert np.all(np.abs(dq) <= eq + 1e-12)
+        # and they are not vacuous: within a modest factor of the gradients' own size
+        assert ev.max() < 50 * np.abs(dv).max() and ek.max() < 200 * np.abs(dk).max()
