@@ -24,6 +24,10 @@
 // would be about Sk / 128 times the size of dQ), no zeroed accumulator, and
 // bitwise-reproducible results.
 //
+// Both kernels run two work-groups of four waves per CU. At d = 128 the
+// dK/dV kernel keeps its 128 V rows as a resident LDS tile (read as the dP
+// operand) instead of registers, which fits that register budget.
+//
 // Both main kernels use the forward's swap-AB orientation for the tile they
 // own: the owned rows (keys in bwd_dkdv, queries in bwd_dq) are the MFMA N
 // dimension held in registers, one row per lane, and the streamed tile is
@@ -46,6 +50,12 @@ namespace attn {
 namespace {
 
 constexpr float kLog2e = 1.44269504088896340736f;
+
+// Where the next step's global loads are issued. At d = 64 after the
+// probabilities are formed (shorter register lifetimes, measured faster); at
+// d = 128 at the top of the step (the later point raises the peak register
+// count past the two-work-groups-per-CU budget).
+template <int D> constexpr bool kLateLoads = D == 64;
 
 __device__ __forceinline__ int pi_row(int i) { return (i & ~12) | ((i >> 1) & 4) | ((i << 1) & 8); }
 
@@ -130,7 +140,7 @@ constexpr int kKT = 128;  // keys per dK/dV work-group
 constexpr int kQB = 32;   // query rows per dK/dV step
 
 template <int D, bool F16>
-__global__ void __launch_bounds__(256, D == 128 ? 1 : 2)
+__global__ void __launch_bounds__(256, 2)
 bwd_dkdv(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
          const uint16_t *__restrict__ dout, const float *__restrict__ l2ws, const float *__restrict__ dws,
          uint16_t *__restrict__ dk, uint16_t *__restrict__ dv, int Sq, int Sq_pad, int Sk, int Hq, int Hkv,
@@ -139,6 +149,9 @@ bwd_dkdv(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const u
   constexpr int QT = kQB * D;                 // one Q (or dO) tile, elements
   constexpr int LPT = kQB * CH / 256;         // 16-byte chunks per thread per tile
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * QT];  // {Q, dO} x 2 slots
+  __shared__ __attribute__((aligned(16))) float stat[2][2][kQB];       // {L2, D} of the step's rows x 2 slots
+  constexpr bool kVinLds = D == 128;  // V rows as an LDS tile instead of registers (register budget)
+  __shared__ __attribute__((aligned(16))) uint16_t vres[kVinLds ? kKT * D : 8];
 
   const int x = blockIdx.x;
   const int kt = x / BHkv;  // key tile 0 first: under a causal mask it has the most queries
@@ -152,14 +165,24 @@ bwd_dkdv(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const u
   const int off = Sk - Sq;
 
   // This lane's K and V row as B operands (d contracted), zero past Sk.
-  uint4 kop[KST], vop[KST];
+  uint4 kop[KST], vop[kVinLds ? 1 : KST];
   {
     const size_t roff = ((size_t)((size_t)b * Sk + (key < Sk ? key : 0)) * Hkv + g) * D;
 #pragma unroll
     for (int kk = 0; kk < KST; ++kk) {
       const bool ok = key < Sk;
       kop[kk] = ok ? ldg16(k + roff + (2 * kk + hl) * 8) : make_uint4(0, 0, 0, 0);
-      vop[kk] = ok ? ldg16(v + roff + (2 * kk + hl) * 8) : make_uint4(0, 0, 0, 0);
+      if constexpr (!kVinLds) vop[kk] = ok ? ldg16(v + roff + (2 * kk + hl) * 8) : make_uint4(0, 0, 0, 0);
+    }
+    if constexpr (kVinLds) {
+      // The work-group's 128 V rows, swizzled like the streamed tiles; read
+      // row-wise (16 consecutive rows per chunk) as the dP operand.
+      const size_t vbase = ((size_t)b * Sk * Hkv + g) * D;
+      for (int c = tid; c < kKT * CH; c += 256) {
+        const int r = c / CH, ch = c % CH, kr = k0 + r;
+        const uint4 val = kr < Sk ? ldg16(v + vbase + (size_t)kr * Hkv * D + ch * 8) : make_uint4(0, 0, 0, 0);
+        sts16(vres + tile_off<D>(r, ch), val);
+      }
     }
   }
   f32x16 dkT[MT], dvT[MT];
@@ -177,9 +200,13 @@ bwd_dkdv(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const u
   const size_t rstride = (size_t)Hq * D;
   const int tg = tid, trow = tg / CH, tch = tg % CH;
   uint4 sq[LPT], sdo[LPT];
+  float4 sst;  // threads 0-15: four L2 (0-7) or D (8-15) values of the step's rows
   auto load_step = [&](int st) {
     const int hh = st / (nqb - ib0), ib = ib0 + st % (nqb - ib0);
     const int h = g * G + hh;
+    if (tid < 16)
+      sst = *reinterpret_cast<const float4 *>((tid < 8 ? l2ws : dws) + ((size_t)b * Hq + h) * Sq_pad + ib * kQB +
+                                              4 * (tid & 7));
     const long long base = ((long long)b * Sq * Hq + h) * D + (long long)ib * kQB * rstride;
     const long long left = ((long long)Sq * Hq - h) * D * 2 - (long long)ib * kQB * rstride * 2;
     const auto rq = buffer_rsrc(q + base, left), rd = buffer_rsrc(dout + base, left);
@@ -198,6 +225,7 @@ bwd_dkdv(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const u
       sts16(qt + tile_off<D>(r, tch), sq[i]);
       sts16(dt + tile_off<D>(r, tch), sdo[i]);
     }
+    if (tid < 16) *reinterpret_cast<float4 *>(&stat[slot][tid >> 3][4 * (tid & 7)]) = sst;
   };
 
   if (nsteps > 0) {
@@ -206,24 +234,29 @@ bwd_dkdv(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const u
   }
   __syncthreads();
   for (int st = 0; st < nsteps; ++st) {
-    if (st + 1 < nsteps) load_step(st + 1);
-    const int hh = st / (nqb - ib0), ib = ib0 + st % (nqb - ib0);
-    const int h = g * G + hh;
+    if constexpr (!kLateLoads<D>) {
+      if (st + 1 < nsteps) load_step(st + 1);
+    }
+    const int ib = ib0 + st % (nqb - ib0);
     const int i0 = ib * kQB;
     const uint16_t *qt = smem + (st & 1) * 2 * QT, *dt = qt + QT;
     // Skip when every query of the step is before the wave's first visible one.
-    if (i0 + kQB - 1 >= wave_first_i && kw0 < Sk) {
+    const bool active = i0 + kQB - 1 >= wave_first_i && kw0 < Sk;
+    if (active) {
       f32x16 S, dP;
 #pragma unroll
       for (int r = 0; r < 16; ++r) S[r] = 0.f, dP[r] = 0.f;
 #pragma unroll
       for (int kk = 0; kk < KST; ++kk) {
         S = mma32<F16>(tile_row_operand<D>(qt, lane, 0, kk), kop[kk], S);
-        dP = mma32<F16>(tile_row_operand<D>(dt, lane, 0, kk), vop[kk], dP);
+        uint4 vb;
+        if constexpr (kVinLds) vb = lds16(vres + tile_off<D>(32 * w + n, 2 * kk + hl));
+        else vb = vop[kk];
+        dP = mma32<F16>(tile_row_operand<D>(dt, lane, 0, kk), vb, dP);
       }
       // Register r holds query i0 + 16 (r / 8) + 8 hl + r % 8.
-      const float *l2p = l2ws + ((size_t)b * Hq + h) * Sq_pad + i0 + 8 * hl;
-      const float *dp = dws + ((size_t)b * Hq + h) * Sq_pad + i0 + 8 * hl;
+      const float *l2p = &stat[st & 1][0][8 * hl];
+      const float *dp = &stat[st & 1][1][8 * hl];
       float l2v[16], dv_[16];
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf)
@@ -255,6 +288,9 @@ bwd_dkdv(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const u
         pS[hf] = make_uint4(pack2<F16>(sv[0], sv[1]), pack2<F16>(sv[2], sv[3]), pack2<F16>(sv[4], sv[5]),
                             pack2<F16>(sv[6], sv[7]));
       }
+      if constexpr (kLateLoads<D>) {
+        if (st + 1 < nsteps) load_step(st + 1);
+      }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -262,6 +298,9 @@ bwd_dkdv(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const u
           dvT[mt] = mma32<F16>(tile_tr_operand<D>(dt, lane, ks, mt), pP[ks], dvT[mt]);
           dkT[mt] = mma32<F16>(tile_tr_operand<D>(qt, lane, ks, mt), pS[ks], dkT[mt]);
         }
+    }
+    if constexpr (kLateLoads<D>) {
+      if (!active && st + 1 < nsteps) load_step(st + 1);
     }
     if (st + 1 < nsteps) store_step((st + 1) & 1);
     __syncthreads();
@@ -289,7 +328,7 @@ constexpr int kQT = 128;  // query rows per dQ work-group
 constexpr int kKB = 64;   // keys per dQ step
 
 template <int D, bool F16>
-__global__ void __launch_bounds__(256, D == 128 ? 1 : 2)
+__global__ void __launch_bounds__(256, 2)
 bwd_dq(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
        const uint16_t *__restrict__ dout, const float *__restrict__ l2ws, const float *__restrict__ dws,
        uint16_t *__restrict__ dq, int Sq, int Sq_pad, int Sk, int Hq, int Hkv, int causal, float scale_log2,
@@ -365,10 +404,13 @@ bwd_dq(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uin
   }
   __syncthreads();
   for (int j = 0; j < nblk; ++j) {
-    if (j + 1 < nblk) load_blk(j + 1);
+    if constexpr (!kLateLoads<D>) {
+      if (j + 1 < nblk) load_blk(j + 1);
+    }
     const int j0 = j * kKB;
     const uint16_t *ktl = smem + (j & 1) * 2 * KTL, *vtl = ktl + KTL;
-    if (j0 < wave_kend) {
+    const bool active = j0 < wave_kend;
+    if (active) {
       f32x16 S[2], dP[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
@@ -398,10 +440,16 @@ bwd_dq(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uin
           pS[2 * t + hf] = make_uint4(pack2<F16>(sv8[0], sv8[1]), pack2<F16>(sv8[2], sv8[3]),
                                       pack2<F16>(sv8[4], sv8[5]), pack2<F16>(sv8[6], sv8[7]));
         }
+      if constexpr (kLateLoads<D>) {
+        if (j + 1 < nblk) load_blk(j + 1);
+      }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) dqT[mt] = mma32<F16>(tile_tr_operand<D>(ktl, lane, ks, mt), pS[ks], dqT[mt]);
+    }
+    if constexpr (kLateLoads<D>) {
+      if (!active && j + 1 < nblk) load_blk(j + 1);
     }
     if (j + 1 < nblk) store_blk((j + 1) & 1);
     __syncthreads();
