@@ -5,18 +5,21 @@ A step is one pass of the whole path over one batch of synthetic input:
   * GQA decode on the headline workload (batch 32, 64 query / 8 KV heads,
     d = 128, one new token, KV lengths uniform in [1024, 8192]): split-KV
     kernel + combine, through the C ABI;
-  * causal prefill (batch 2, 32 heads, d = 128, S = 8192) through attn_fwd.
+  * causal prefill (batch 2, 32 heads, d = 128, S = 8192) through attn_fwd;
+  * the backward pass of that prefill (dQ, dK, dV from its O and LSE and a
+    synthetic dO) through attn_bwd.
 The headline `value` is decode KV-read bandwidth: algorithmic K+V bytes
 (sum_b L_b * Hkv * 4d) over the measured duration of the decode call, timed
 with HIP events on the stream the kernels run on. Prefill TFLOP/s (exact causal
-FLOPs, 4 d per visible query-key pair) is reported beside it.
+FLOPs, 4 d per visible query-key pair) is reported beside it, and backward
+TFLOP/s counted, as the backward page does, as 2.5 times the forward FLOPs.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-backward]
 Prints one JSON line.
 
 HBM traffic (roofline.traffic) comes from two rocprofv3 counter passes over
 `bench.py --counter-run` (one 1 GiB device copy for calibration, then one
-decode call and one prefill call, nothing timed):
+decode call, one prefill call and one backward call, nothing timed):
   rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT -o fetch -- python bench.py --counter-run
   rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT -o write -- python bench.py --counter-run
   python bench.py --ingest-counters OUT/fetch_counter_collection.csv OUT/write_counter_collection.csv
@@ -41,6 +44,7 @@ HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published
 DECODE_SOURCES = ["attention_attn_decode_amd/csrc/decode.hip", "attention_attn_decode_amd/csrc/attn_device.h"]
 FWD_SOURCES = ["attention_attn_decode_amd/csrc/fwd.hip", "attention_attn_decode_amd/csrc/attn_device.h"]
+BWD_SOURCES = ["attention_attn_decode_amd/csrc/bwd.hip", "attention_attn_decode_amd/csrc/attn_device.h"]
 COUNTERS = os.path.join(ROOT, "profiles", "hbm_traffic_counters.json")
 
 
@@ -84,6 +88,8 @@ TRAFFIC_KERNELS = {  # stored key -> (kernel-name prefixes, sources, workload)
     "attn_decode": (("decode_stream<", "combine_pieces<"), DECODE_SOURCES,
                     "gqa-decode b=32 hq=64 hkv=8 d=128 sq=1 kv_len~U[1024,8192] (seed 1001)"),
     "fwd_pp": (("fwd_pp<",), FWD_SOURCES, "causal-prefill b=2 h=32 d=128 s=8192 (seed 1004)"),
+    "attn_bwd": (("bwd_pre<", "bwd_dkdv<", "bwd_dq<"), BWD_SOURCES,
+                 "causal-prefill backward b=2 h=32 d=128 s=8192 (seed 1004, dO seed 1005)"),
 }
 
 
@@ -163,6 +169,7 @@ def main():
     ap.add_argument("--num-splits", type=int, default=0, help="decode pieces per KV head (0 = automatic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--counter-run", action="store_true",
                     help="one copy, one decode and one prefill dispatch for rocprofv3 --pmc passes")
     ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
@@ -221,7 +228,15 @@ def main():
         qp, kp, vp = to_dev(xp.q), to_dev(xp.k), to_dev(xp.v)
         op = torch.empty_like(qp)
         lsep = torch.empty((pc.batch, pc.n_q_heads, pc.seqlen), dtype=torch.float32, device=dev)
+        run_backward = not args.no_backward
+        if run_backward:
+            dop = to_dev(wl.make_grad_out(xp.q, 1005))
+            dqp, dkp, dvp = torch.empty_like(qp), torch.empty_like(kp), torch.empty_like(vp)
+            wsb = torch.empty(aa.attn_bwd_workspace_size(pc.batch, pc.n_q_heads, pc.seqlen), dtype=torch.uint8,
+                              device=dev)
         del xp
+    else:
+        run_backward = False
     setup_s = time.perf_counter() - t0
 
     stream = torch.cuda.current_stream()
@@ -236,6 +251,8 @@ def main():
         aa.attn_decode(q, k, v, sl, od, lsed, workspace=ws, num_splits=args.num_splits, stream=stream)
         if run_prefill:
             aa.attn_fwd(qp, kp, vp, op, lsep, causal=True, stream=stream)
+        if run_backward:
+            aa.attn_bwd(qp, kp, vp, op, lsep, dop, dqp, dkp, dvp, wsb, causal=True, stream=stream)
         torch.cuda.synchronize()
         print("counter run done", flush=True)
         return
@@ -251,11 +268,15 @@ def main():
             aa.attn_fwd(qp, kp, vp, op, lsep, causal=True, stream=stream)
         if evs:
             evs[2].record(stream)
+        if run_backward:
+            aa.attn_bwd(qp, kp, vp, op, lsep, dop, dqp, dkp, dvp, wsb, causal=True, stream=stream)
+        if evs:
+            evs[3].record(stream)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(args.steps):
@@ -264,6 +285,7 @@ def main():
     wall = time.perf_counter() - t_start
     dec_ms = [e[0].elapsed_time(e[1]) for e in events]
     pre_ms = [e[1].elapsed_time(e[2]) for e in events]
+    bwd_ms = [e[2].elapsed_time(e[3]) for e in events]
     dec_mean = statistics.fmean(dec_ms)
     pre_mean = statistics.fmean(pre_ms) if run_prefill else 0.0
 
@@ -306,6 +328,7 @@ def main():
             "kv_tokens": int(xd.seqlens.sum()),
             "pieces_per_kv_head": pieces,
             "prefill_workload": "causal-prefill b=2 h=32 d=128 s=8192 (seed 1004)" if run_prefill else None,
+            "backward_workload": "backward of that prefill, dO seed 1005" if run_backward else None,
             "parallelism": "single-gpu",
             "device": props.name,
             "cus": props.multi_processor_count,
@@ -347,6 +370,23 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(tf / BF16_PEAK_TFLOPS, 4),
             "traffic": measured_traffic("fwd_pp", source_hash(FWD_SOURCES), None),
+        }
+    if run_backward:
+        bwd_mean = statistics.fmean(bwd_ms)
+        fl = 2.5 * causal_flops(pc.batch, pc.n_q_heads, pc.seqlen, pc.d)
+        tf = fl / (bwd_mean * 1e-3) / 1e12
+        result["backward"] = {
+            "bound": "mfma",
+            "kernel": "attn_bwd = bwd_pre + bwd_dkdv + bwd_dq",
+            "ms_mean": round(bwd_mean, 5),
+            "ms_median": round(statistics.median(bwd_ms), 5),
+            "flops": int(fl),
+            "flops_note": "2.5 x the causal forward FLOPs (five products per visible pair)",
+            "achieved": round(tf, 2),
+            "peak": BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+            "traffic": measured_traffic("attn_bwd", source_hash(BWD_SOURCES), None),
         }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline_decode(xd, d)
