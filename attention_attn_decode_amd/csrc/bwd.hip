@@ -44,6 +44,8 @@
 // the forward: query i sees keys j <= i + Sk - Sq. Masked pairs, rows past Sq
 // and keys past Sk get P = dS = 0 by selection, so no infinity or NaN from
 // padding reaches a product.
+#include <type_traits>
+
 #include "attn_device.h"
 
 namespace attn {
@@ -56,6 +58,12 @@ constexpr float kLog2e = 1.44269504088896340736f;
 // d = 128 at the top of the step (the later point raises the peak register
 // count past the two-work-groups-per-CU budget).
 template <int D> constexpr bool kLateLoads = D == 64;
+
+// A separate mask-free path for tiles wholly inside the visible region. At
+// d = 64 the per-element mask is a large share of the step's vector work (the
+// products are short); at d = 128 the second copy of the loop body pushes the
+// register count past the budget, so every tile takes the masked path.
+template <int D> constexpr bool kUnmaskedPath = D == 64;
 
 __device__ __forceinline__ int pi_row(int i) { return (i & ~12) | ((i >> 1) & 4) | ((i << 1) & 8); }
 
@@ -271,22 +279,48 @@ bwd_dkdv(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const u
         }
       const int lim = causal ? key - off : -0x40000000;  // query i sees this key iff i >= lim
       uint4 pP[2], pS[2];
+      auto probs = [&](auto masked) {  // the d = 64 form (see kUnmaskedPath)
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        float pv[8], sv[8];
+        for (int hf = 0; hf < 2; ++hf) {
+          float pv[8], sv[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int r = 8 * hf + e;
-          const int qi = i0 + 16 * hf + 8 * hl + e;
-          const bool vis = key < Sk && qi < Sq && qi >= lim;
-          const float p = vis ? exp2_hw(__builtin_fmaf(S[r], scale_log2, -l2v[r])) : 0.f;
-          pv[e] = p;
-          sv[e] = vis ? p * (dP[r] - dv_[r]) : 0.f;
+          for (int e = 0; e < 8; ++e) {
+            const int r = 8 * hf + e;
+            const int qi = i0 + 16 * hf + 8 * hl + e;
+            const bool vis = !decltype(masked)::value || (key < Sk && qi < Sq && qi >= lim);
+            const float p = vis ? exp2_hw(__builtin_fmaf(S[r], scale_log2, -l2v[r])) : 0.f;
+            pv[e] = p;
+            sv[e] = vis ? p * (dP[r] - dv_[r]) : 0.f;
+          }
+          pP[hf] = make_uint4(pack2<F16>(pv[0], pv[1]), pack2<F16>(pv[2], pv[3]), pack2<F16>(pv[4], pv[5]),
+                              pack2<F16>(pv[6], pv[7]));
+          pS[hf] = make_uint4(pack2<F16>(sv[0], sv[1]), pack2<F16>(sv[2], sv[3]), pack2<F16>(sv[4], sv[5]),
+                              pack2<F16>(sv[6], sv[7]));
         }
-        pP[hf] = make_uint4(pack2<F16>(pv[0], pv[1]), pack2<F16>(pv[2], pv[3]), pack2<F16>(pv[4], pv[5]),
-                            pack2<F16>(pv[6], pv[7]));
-        pS[hf] = make_uint4(pack2<F16>(sv[0], sv[1]), pack2<F16>(sv[2], sv[3]), pack2<F16>(sv[4], sv[5]),
-                            pack2<F16>(sv[6], sv[7]));
+      };
+      // A step wholly inside the visible region (every key of the wave seen
+      // by every row, no padding) needs no mask.
+      if constexpr (kUnmaskedPath<D>) {
+        if (kw0 + 31 < Sk && i0 + kQB - 1 < Sq && (!causal || i0 >= kw0 + 31 - off)) probs(std::false_type{});
+        else probs(std::true_type{});
+      } else {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          float pv[8], sv[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int r = 8 * hf + e;
+            const int qi = i0 + 16 * hf + 8 * hl + e;
+            const bool vis = key < Sk && qi < Sq && qi >= lim;
+            const float p = vis ? exp2_hw(__builtin_fmaf(S[r], scale_log2, -l2v[r])) : 0.f;
+            pv[e] = p;
+            sv[e] = vis ? p * (dP[r] - dv_[r]) : 0.f;
+          }
+          pP[hf] = make_uint4(pack2<F16>(pv[0], pv[1]), pack2<F16>(pv[2], pv[3]), pack2<F16>(pv[4], pv[5]),
+                              pack2<F16>(pv[6], pv[7]));
+          pS[hf] = make_uint4(pack2<F16>(sv[0], sv[1]), pack2<F16>(sv[2], sv[3]), pack2<F16>(sv[4], sv[5]),
+                              pack2<F16>(sv[6], sv[7]));
+        }
       }
       if constexpr (kLateLoads<D>) {
         if (st + 1 < nsteps) load_step(st + 1);
@@ -424,22 +458,32 @@ bwd_dq(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uin
       }
       // Register r of tile t holds key j0 + 32 t + 16 (r / 8) + 8 hl + r % 8.
       uint4 pS[4];
+      auto probs = [&](auto masked) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          float sv8[8];
+          for (int hf = 0; hf < 2; ++hf) {
+            float sv8[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int r = 8 * hf + e;
-            const int kj = j0 + 32 * t + 16 * hf + 8 * hl + e;
-            const bool vis = kj < Sk && kj <= lim && qrow < Sq;
-            const float p = vis ? exp2_hw(__builtin_fmaf(S[t][r], scale_log2, -l2)) : 0.f;
-            sv8[e] = vis ? p * (dP[t][r] - Dr) : 0.f;
+            for (int e = 0; e < 8; ++e) {
+              const int r = 8 * hf + e;
+              const int kj = j0 + 32 * t + 16 * hf + 8 * hl + e;
+              const bool vis = !decltype(masked)::value || (kj < Sk && kj <= lim && qrow < Sq);
+              const float p = vis ? exp2_hw(__builtin_fmaf(S[t][r], scale_log2, -l2)) : 0.f;
+              sv8[e] = vis ? p * (dP[t][r] - Dr) : 0.f;
+            }
+            pS[2 * t + hf] = make_uint4(pack2<F16>(sv8[0], sv8[1]), pack2<F16>(sv8[2], sv8[3]),
+                                        pack2<F16>(sv8[4], sv8[5]), pack2<F16>(sv8[6], sv8[7]));
           }
-          pS[2 * t + hf] = make_uint4(pack2<F16>(sv8[0], sv8[1]), pack2<F16>(sv8[2], sv8[3]),
-                                      pack2<F16>(sv8[4], sv8[5]), pack2<F16>(sv8[6], sv8[7]));
-        }
+      };
+      // A block wholly inside the visible region of every row of the wave
+      // needs no mask.
+      if constexpr (kUnmaskedPath<D>) {
+        if (j0 + kKB - 1 < Sk && r0 + 31 < Sq && (!causal || j0 + kKB - 1 <= r0 + off)) probs(std::false_type{});
+        else probs(std::true_type{});
+      } else {
+        probs(std::true_type{});
+      }
       if constexpr (kLateLoads<D>) {
         if (j + 1 < nblk) load_blk(j + 1);
       }
