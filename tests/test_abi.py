@@ -112,3 +112,30 @@ def test_null_pointers_are_rejected_before_any_device_work():
     # workspace too small for a multi-piece plan
     assert L.attn_decode_ex(fake, fake, fake, fake, fake, None, 8, 1, 64, 1, 1, 4096, fake, 16, None, 4) == aa.ATTN_ERR_WORKSPACE
     assert L.attn_decode_ex(fake, fake, fake, fake, fake, None, 8, 1, 64, 1, 1, 4096, fake, 16, None, -1) == aa.ATTN_ERR_INVALID
+
+
+def test_backward_workspace_size_formula():
+    ensure_built()
+    for B, Hq, Sq in ((1, 1, 1), (2, 32, 8192), (3, 5, 129), (1, 64, 128)):
+        pad = -(-Sq // 128) * 128
+        assert aa.attn_bwd_workspace_size(B, Hq, Sq) == 2 * B * Hq * pad * 4
+    assert aa.attn_bwd_workspace_size(0, 8, 16) == 0 and aa.attn_bwd_workspace_size(1, 8, -1) == 0
+
+
+def test_backward_validation_before_any_device_work():
+    L = ensure_built()
+    f, odd = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x1002)
+    ws_ok = aa.attn_bwd_workspace_size(1, 8, 16)
+
+    def call(q=f, k=f, v=f, o=f, lse=f, do=f, dq=f, dk=f, dv=f, causal=1, B=1, Sq=16, Sk=16, Hq=8, Hkv=8, d=64,
+             ws=f, wsb=ws_ok, fn=L.attn_bwd):
+        return fn(q, k, v, o, lse, do, dq, dk, dv, causal, B, Sq, Sk, Hq, Hkv, d, ws, wsb, None)
+
+    for name in ("q", "k", "v", "o", "lse", "do", "dq", "dk", "dv", "ws"):
+        assert call(**{name: None}) == aa.ATTN_ERR_INVALID, name
+    assert call(B=0) == aa.ATTN_ERR_INVALID and call(Sk=-1) == aa.ATTN_ERR_INVALID
+    assert call(Hkv=3) == aa.ATTN_ERR_INVALID           # Hq % Hkv != 0
+    assert call(d=96) == aa.ATTN_ERR_UNSUPPORTED
+    assert call(dk=odd) == aa.ATTN_ERR_MISALIGNED and call(lse=ctypes.c_void_p(0x1001)) == aa.ATTN_ERR_MISALIGNED
+    assert call(wsb=ws_ok - 4) == aa.ATTN_ERR_WORKSPACE
+    assert call(fn=L.attn_bwd_f16, d=80) == aa.ATTN_ERR_UNSUPPORTED
