@@ -20,6 +20,7 @@ from .attention import (  # noqa: F401
     to_f64,
     attention,
     attention_rows,
+    attention_varlen,
     probabilities,
     split_partials,
     combine_partials,

@@ -213,3 +213,25 @@ def combine_partials(ms, ls, Os):
         ell += w * ls[i]
         acc += w * Os[i]
     return acc / ell, math.log(2.0) * (M + math.log2(ell))
+
+
+def attention_varlen(q, k, v, cu_q, cu_k, causal=True, dtype="bf16"):
+    """Reference attention over a packed variable-length batch.
+
+    q: uint16 [total_q, Hq, d]; k, v: uint16 [total_k, Hkv, d]; cu_q, cu_k:
+    int[B + 1] row offsets of each sequence. Each sequence is an independent
+    prefill (bottom-right causal within it when causal). Returns
+    (O fp64 [total_q, Hq, d], LSE fp64 [Hq, total_q]).
+    """
+    tq, Hq, d = q.shape
+    O = np.zeros((tq, Hq, d), dtype=np.float64)
+    LSE = np.full((Hq, tq), -np.inf, dtype=np.float64)
+    for b in range(len(cu_q) - 1):
+        s0, s1 = int(cu_q[b]), int(cu_q[b + 1])
+        t0, t1 = int(cu_k[b]), int(cu_k[b + 1])
+        if s1 <= s0:
+            continue
+        o, lse = attention(q[None, s0:s1], k[None, t0:t1], v[None, t0:t1], None, causal, dtype=dtype)
+        O[s0:s1] = o[0]
+        LSE[:, s0:s1] = lse[0]
+    return O, LSE

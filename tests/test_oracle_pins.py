@@ -309,3 +309,38 @@ def test_f16_one_hot_limit():
     x.k[0, 4, 0] = wl.f32_to_f16_bits((8.0 * qv).astype(np.float32))
     O, L = oracle.attention(x.q, x.k, x.v, x.seqlens, True, dtype="f16")
     assert np.abs(O[0, 0, 0] - oracle.f16_bits_to_f64(x.v[0, 4, 0])).max() <= 1e-6
+
+
+# --- variable-length batches ---------------------------------------------------
+
+def test_varlen_equal_lengths_match_the_batched_oracle():
+    """A packed batch of equal-length sequences is the batched [B, S, H, d] problem."""
+    B, S, Hq, Hkv, d = 3, 37, 4, 2, 16
+    x = wl.make_varlen([S] * B, [S] * B, Hq, Hkv, d, seed=91)
+    for causal in (True, False):
+        O, L = oracle.attention_varlen(x.q, x.k, x.v, x.cu_q, x.cu_k, causal)
+        Ob, Lb = oracle.attention(x.q.reshape(B, S, Hq, d), x.k.reshape(B, S, Hkv, d), x.v.reshape(B, S, Hkv, d),
+                                  None, causal)
+        assert np.array_equal(O, Ob.reshape(B * S, Hq, d))
+        assert np.array_equal(L, Lb.transpose(1, 0, 2).reshape(Hq, B * S))
+
+
+def test_varlen_sequences_are_independent_and_edges_hold():
+    """Each sequence sees only its own keys (a needle in another sequence is invisible);
+    an empty key range gives O = 0 and LSE = -inf; Sq > Sk puts the causal diagonal bottom-right."""
+    lq, lk = [5, 0, 7, 3], [5, 4, 3, 0]
+    x = wl.make_varlen(lq, lk, 2, 1, 8, seed=92)
+    O, L = oracle.attention_varlen(x.q, x.k, x.v, x.cu_q, x.cu_k, True)
+    # sequence 3 has no keys
+    s0, s1 = x.cu_q[3], x.cu_q[4]
+    assert np.all(O[s0:s1] == 0) and np.all(np.isneginf(L[:, s0:s1]))
+    # sequence 2: 7 queries over 3 keys, bottom-right: query t sees keys j <= t - 4
+    s0 = x.cu_q[2]
+    assert np.all(np.isneginf(L[:, s0:s0 + 4])) and np.isfinite(L[:, s0 + 4:s0 + 7]).all()
+    # row 4 of sequence 2 sees exactly key 0 of that sequence: O = v_0
+    assert np.array_equal(O[s0 + 4, 0], f64(x.v[x.cu_k[2], 0]))
+    # changing sequence 0's keys leaves sequence 2 unchanged
+    k2 = x.k.copy()
+    k2[x.cu_k[0]:x.cu_k[1]] = bits(np.full((5, 1, 8), 3.0))
+    O2, _ = oracle.attention_varlen(x.q, k2, x.v, x.cu_q, x.cu_k, True)
+    assert np.array_equal(O2[x.cu_q[2]:], O[x.cu_q[2]:])

@@ -197,6 +197,32 @@ def make_prefill(batch, n_q_heads, n_kv_heads, d, seqlen_q, seqlen_k, seed,
     return PrefillInputs(q, k, v, dict(seed=seed), dtype)
 
 
+@dataclass
+class VarlenInputs:
+    q: np.ndarray        # uint16 [total_q, Hq, d], sequences packed back to back
+    k: np.ndarray        # uint16 [total_k, Hkv, d]
+    v: np.ndarray        # uint16 [total_k, Hkv, d]
+    cu_q: np.ndarray     # int32 [B + 1], cu_q[b] = first query row of sequence b
+    cu_k: np.ndarray     # int32 [B + 1]
+    meta: dict = field(default_factory=dict)
+    dtype: str = "bf16"
+
+
+def make_varlen(lens_q, lens_k, n_q_heads, n_kv_heads, d, seed, dtype="bf16") -> VarlenInputs:
+    """Packed variable-length batch: sequence b has lens_q[b] queries and lens_k[b] keys."""
+    lq = np.asarray(lens_q, dtype=np.int64)
+    lk = np.asarray(lens_k, dtype=np.int64)
+    if lq.shape != lk.shape or (lq < 0).any() or (lk < 0).any():
+        raise ValueError("lens_q and lens_k must be non-negative and of equal length")
+    cu_q = np.concatenate([[0], np.cumsum(lq)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(lk)]).astype(np.int32)
+    tq, tk = int(cu_q[-1]), int(cu_k[-1])
+    q = normal_bits(seed, TID_Q, tq * n_q_heads * d, dtype=dtype).reshape(tq, n_q_heads, d)
+    k = normal_bits(seed, TID_K, tk * n_kv_heads * d, dtype=dtype).reshape(tk, n_kv_heads, d)
+    v = normal_bits(seed, TID_V, tk * n_kv_heads * d, dtype=dtype).reshape(tk, n_kv_heads, d)
+    return VarlenInputs(q, k, v, cu_q, cu_k, dict(seed=seed), dtype)
+
+
 def make_grad_out(q: np.ndarray, seed: int, dtype: str = "bf16") -> np.ndarray:
     """Output gradient dO shaped like q: N(0,1) draws of stream (seed, TID_DO)."""
     return normal_bits(seed, TID_DO, q.size, dtype=dtype).reshape(q.shape)
