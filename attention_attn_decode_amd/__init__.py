@@ -27,7 +27,8 @@ ATTN_MAX_BATCH = 8192
 
 # Every symbol include/attn.h declares.
 EXPORTS = ("attn_decode_plan", "attn_decode_workspace_size", "attn_decode", "attn_decode_ex",
-           "attn_decode_f16", "attn_fwd", "attn_fwd_f16", "attn_bwd_workspace_size", "attn_bwd",
+           "attn_decode_f16", "attn_fwd", "attn_fwd_f16", "attn_fwd_varlen", "attn_fwd_varlen_f16",
+           "attn_bwd_workspace_size", "attn_bwd",
            "attn_bwd_f16", "attn_status_string", "attn_version")
 
 _lib = None
@@ -61,6 +62,9 @@ def lib() -> ctypes.CDLL:
         getattr(L, name).restype = i32
     for name in ("attn_fwd", "attn_fwd_f16"):
         getattr(L, name).argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp]
+        getattr(L, name).restype = i32
+    for name in ("attn_fwd_varlen", "attn_fwd_varlen_f16"):
+        getattr(L, name).argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, vp]
         getattr(L, name).restype = i32
     L.attn_bwd_workspace_size.argtypes = [i32, i32, i32]
     L.attn_bwd_workspace_size.restype = sz
@@ -195,6 +199,34 @@ def attn_fwd(q, k, v, o, lse=None, causal=True, stream=None):
             _stream_ptr(stream))
     if st != ATTN_OK:
         raise AttnError(st, "attn_fwd")
+
+
+def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, o, max_seqlen_q, lse=None, causal=True, stream=None):
+    """Prefill forward over a packed variable-length batch. q, o: bf16 or fp16 [total_q, Hq, d];
+    k, v: same type [total_k, Hkv, d]; cu_seqlens_q/k: int32 [B + 1] device offsets;
+    lse: fp32 [Hq, total_q] or None; max_seqlen_q: at least the longest query length."""
+    import torch
+    et, f16 = _elem(q)
+    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
+        _check(t, nm, et, 3)
+    _check(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1)
+    _check(cu_seqlens_k, "cu_seqlens_k", torch.int32, 1)
+    tq, Hq, d = q.shape
+    tk, Hkv, dk = k.shape
+    B = cu_seqlens_q.shape[0] - 1
+    if tuple(v.shape) != tuple(k.shape) or dk != d or tuple(o.shape) != tuple(q.shape):
+        raise ValueError("shape mismatch among q, k, v, o")
+    if cu_seqlens_k.shape[0] != B + 1 or B < 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both have B + 1 entries, B >= 1")
+    if lse is not None:
+        _check(lse, "lse", torch.float32, 2)
+        if tuple(lse.shape) != (Hq, tq):
+            raise ValueError("lse must be [Hq, total_q]")
+    fn = lib().attn_fwd_varlen_f16 if f16 else lib().attn_fwd_varlen
+    st = fn(_ptr(q), _ptr(k) if tk else None, _ptr(v) if tk else None, _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+            _ptr(o), _ptr(lse), 1 if causal else 0, B, int(max_seqlen_q), tq, tk, Hq, Hkv, d, _stream_ptr(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd_varlen")
 
 
 def attn_bwd_workspace_size(batch, n_q_heads, seqlen_q) -> int:

@@ -14,9 +14,9 @@ hipError_t launch_decode(const void *q, const void *k, const void *v, const int3
                          int batch, int Hq,
                          int Hkv, int d, int sq, int max_len, int pieces, int min_piece,
                          float scale_log2, bool f16, hipStream_t stream);
-hipError_t launch_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int causal,
-                      int batch, int Sq, int Sk, int Hq, int Hkv, int d, float scale_log2, bool f16,
-                      hipStream_t stream);
+hipError_t launch_fwd(const void *q, const void *k, const void *v, void *o, float *lse, const int *cu_q,
+                      const int *cu_k, int total_q, int total_k, int causal, int batch, int Sq, int Sk, int Hq,
+                      int Hkv, int d, float scale_log2, bool f16, hipStream_t stream);
 hipError_t launch_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse, const void *dout,
                       void *dq, void *dk, void *dv, int causal, int batch, int Sq, int Sk, int Hq, int Hkv, int d,
                       float *l2ws, float *dws, bool f16, hipStream_t stream);
@@ -133,8 +133,27 @@ int fwd_impl(const void *q, const void *k, const void *v, void *o, float *lse, i
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (lse && !aligned4(lse)))
     return ATTN_ERR_MISALIGNED;
   const hipError_t err =
-      attn::launch_fwd(q, k, v, o, lse, causal ? 1 : 0, batch, seqlen_q, seqlen_k, n_q_heads,
-                       n_kv_heads, d, scale_log2_for(d), f16, static_cast<hipStream_t>(stream));
+      attn::launch_fwd(q, k, v, o, lse, nullptr, nullptr, 0, 0, causal ? 1 : 0, batch, seqlen_q, seqlen_k,
+                       n_q_heads, n_kv_heads, d, scale_log2_for(d), f16, static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+int fwd_varlen_impl(const void *q, const void *k, const void *v, const int32_t *cu_q, const int32_t *cu_k, void *o,
+                    float *lse, int causal, int batch, int max_seqlen_q, int total_q, int total_k, int n_q_heads,
+                    int n_kv_heads, int d, void *stream, bool f16) {
+  if (!q || !o || !cu_q || !cu_k || (total_k > 0 && (!k || !v))) return ATTN_ERR_INVALID;
+  if (batch <= 0 || max_seqlen_q <= 0 || total_q <= 0 || total_k < 0 || n_q_heads <= 0 || n_kv_heads <= 0)
+    return ATTN_ERR_INVALID;
+  if (n_q_heads % n_kv_heads != 0) return ATTN_ERR_INVALID;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  const long wgs = (long)((max_seqlen_q + 255) / 256) * batch * n_q_heads;
+  if (wgs > 0x7fffffffL || (long long)total_q * n_q_heads > 0x7fffffffLL) return ATTN_ERR_UNSUPPORTED;
+  if (!aligned16(q) || (k && !aligned16(k)) || (v && !aligned16(v)) || !aligned16(o) || (lse && !aligned4(lse)) ||
+      !aligned4(cu_q) || !aligned4(cu_k))
+    return ATTN_ERR_MISALIGNED;
+  const hipError_t err =
+      attn::launch_fwd(q, k, v, o, lse, cu_q, cu_k, total_q, total_k, causal ? 1 : 0, batch, max_seqlen_q, 0,
+                       n_q_heads, n_kv_heads, d, scale_log2_for(d), f16, static_cast<hipStream_t>(stream));
   return err == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
@@ -225,6 +244,20 @@ int attn_fwd_f16(const void *q, const void *k, const void *v, void *o, float *ls
                  int batch, int seqlen_q, int seqlen_k, int n_q_heads, int n_kv_heads, int d,
                  void *stream) {
   return fwd_impl(q, k, v, o, lse, causal, batch, seqlen_q, seqlen_k, n_q_heads, n_kv_heads, d, stream, true);
+}
+
+int attn_fwd_varlen(const void *q, const void *k, const void *v, const int32_t *cu_seqlens_q,
+                    const int32_t *cu_seqlens_k, void *o, float *lse, int causal, int batch, int max_seqlen_q,
+                    int total_q, int total_k, int n_q_heads, int n_kv_heads, int d, void *stream) {
+  return fwd_varlen_impl(q, k, v, cu_seqlens_q, cu_seqlens_k, o, lse, causal, batch, max_seqlen_q, total_q, total_k,
+                         n_q_heads, n_kv_heads, d, stream, false);
+}
+
+int attn_fwd_varlen_f16(const void *q, const void *k, const void *v, const int32_t *cu_seqlens_q,
+                        const int32_t *cu_seqlens_k, void *o, float *lse, int causal, int batch, int max_seqlen_q,
+                        int total_q, int total_k, int n_q_heads, int n_kv_heads, int d, void *stream) {
+  return fwd_varlen_impl(q, k, v, cu_seqlens_q, cu_seqlens_k, o, lse, causal, batch, max_seqlen_q, total_q, total_k,
+                         n_q_heads, n_kv_heads, d, stream, true);
 }
 
 const char *attn_status_string(int status) {

@@ -76,6 +76,7 @@ template <int D, bool F16>
 __global__ void __launch_bounds__(512, 1)
 fwd_pp(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
        const uint16_t *__restrict__ v, uint16_t *__restrict__ o, float *__restrict__ lse,
+       const int *__restrict__ cu_q, const int *__restrict__ cu_k, int total_q, int total_k,
        int Sq, int Sk, int Hq, int Hkv, int causal, float scale_log2, int n_mblocks, int BH) {
   constexpr int BN = 64;
   constexpr int CH = D / 8;        // 16-byte chunks per row
@@ -97,6 +98,22 @@ fwd_pp(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
   const int b = u / Hq, h = u % Hq;
   const int gk = h / (Hq / Hkv);
   const int q0 = mb * kBMP;
+  // Rows of sequence b: dense batches are [B][S] blocks; a packed
+  // variable-length batch gives each sequence's first row in cu_q / cu_k
+  // (clamped to the packed totals, so any offsets stay inside the buffers).
+  // LSE is [B][Hq][Sq] dense, [Hq][total_q] packed.
+  int qbase, kbase, lse_hs;
+  size_t lse_base;
+  if (cu_q != nullptr) {
+    const int a0 = min(max(cu_q[b], 0), total_q), a1 = min(max(cu_q[b + 1], a0), total_q);
+    const int c0 = min(max(cu_k[b], 0), total_k), c1 = min(max(cu_k[b + 1], c0), total_k);
+    qbase = a0, Sq = a1 - a0, kbase = c0, Sk = c1 - c0;
+    lse_base = (size_t)qbase, lse_hs = total_q;
+    if (q0 >= Sq) return;  // the whole work-group: this sequence has fewer query tiles
+  } else {
+    qbase = b * Sq, kbase = b * Sk;
+    lse_base = (size_t)b * Hq * Sq, lse_hs = Sq;
+  }
   // Wave index in a scalar register: every per-wave condition below (group,
   // key range, skipped blocks) is then a uniform branch, and the barriers
   // inside group-dependent code are passed by whole waves only.
@@ -123,7 +140,7 @@ fwd_pp(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
   uint4 qop[KST];
   {
     const bool ok = qrow < Sq;
-    const uint16_t *qp = q + ((size_t)(b * Sq + (ok ? qrow : 0)) * Hq + h) * D;
+    const uint16_t *qp = q + ((size_t)(qbase + (ok ? qrow : 0)) * Hq + h) * D;
 #pragma unroll
     for (int kk = 0; kk < KST; ++kk) qop[kk] = ok ? ldg16(qp + (2 * kk + hl) * 8) : make_uint4(0, 0, 0, 0);
   }
@@ -134,8 +151,8 @@ fwd_pp(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
   // excludes them), and the only per-lane address is a constant offset: no
   // vector address arithmetic per load.
   const size_t rstride = (size_t)Hkv * D;
-  const uint16_t *src = (G == 0 ? k : v) + ((size_t)b * Sk * Hkv + gk) * D;
-  const long long src_bytes = ((long long)Sk * Hkv - gk) * D * 2;  // src to the end of batch b
+  const uint16_t *src = (G == 0 ? k : v) + ((size_t)kbase * Hkv + gk) * D;
+  const long long src_bytes = ((long long)Sk * Hkv - gk) * D * 2;  // src to the end of sequence b
   uint16_t *const dtile = G == 0 ? ktile : vtile;
   const int drow = G == 0 ? KROW : VROW, dsize = G == 0 ? KT : VT;
   const int tg = tid & 255, trow = tg / CH, tcol = (tg % CH) * 8;
@@ -350,7 +367,7 @@ fwd_pp(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
   const float l_col = wave_xor_sum(l_run, 32);
   if (qrow >= Sq) return;
   const float inv = l_col > 0.f ? 1.f / l_col : 0.f;
-  uint16_t *dst = o + ((size_t)(b * Sq + qrow) * Hq + h) * D;
+  uint16_t *dst = o + ((size_t)(qbase + qrow) * Hq + h) * D;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -361,14 +378,17 @@ fwd_pp(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
                      pack2<F16>(oacc[mt][4 * a + 2] * inv, oacc[mt][4 * a + 3] * inv));
     }
   if (lse != nullptr && hl == 0)
-    lse[((size_t)b * Hq + h) * Sq + qrow] = l_col > 0.f ? kLn2 * (m_run + __log2f(l_col)) : kNegInf;
+    lse[lse_base + (size_t)h * lse_hs + qrow] = l_col > 0.f ? kLn2 * (m_run + __log2f(l_col)) : kNegInf;
 }
 
 }  // namespace
 
-hipError_t launch_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int causal,
-                      int batch, int Sq, int Sk, int Hq, int Hkv, int d, float scale_log2, bool f16,
-                      hipStream_t stream) {
+// Dense when cu_q == nullptr (Sq, Sk the per-sequence lengths); packed
+// variable-length otherwise (Sq = the longest query length, which sizes the
+// grid; Sk unused; total_q, total_k the packed row counts).
+hipError_t launch_fwd(const void *q, const void *k, const void *v, void *o, float *lse, const int *cu_q,
+                      const int *cu_k, int total_q, int total_k, int causal, int batch, int Sq, int Sk, int Hq,
+                      int Hkv, int d, float scale_log2, bool f16, hipStream_t stream) {
   const int BH = batch * Hq;
   const int n_mblocks = (Sq + kBMP - 1) / kBMP;
   const dim3 grid(n_mblocks * BH), block(512);
@@ -377,8 +397,8 @@ hipError_t launch_fwd(const void *q, const void *k, const void *v, void *o, floa
   const auto *vv = static_cast<const uint16_t *>(v);
   auto *oo = static_cast<uint16_t *>(o);
   auto run = [&](auto kern) {
-    hipLaunchKernelGGL(kern, grid, block, 0, stream, qq, kk, vv, oo, lse, Sq, Sk, Hq, Hkv, causal, scale_log2,
-                       n_mblocks, BH);
+    hipLaunchKernelGGL(kern, grid, block, 0, stream, qq, kk, vv, oo, lse, cu_q, cu_k, total_q, total_k, Sq, Sk, Hq,
+                       Hkv, causal, scale_log2, n_mblocks, BH);
   };
   if (d == 128) {
     if (f16) run(fwd_pp<128, true>);

@@ -176,6 +176,36 @@ int attn_fwd_f16(const void *q, const void *k, const void *v, void *o, float *ls
                  void *stream);
 
 /*
+ * Prefill forward over a packed variable-length batch (the backward page
+ * sweeps variable-length shapes, [FA4-bwd] §Results): sequence b owns query
+ * rows [cu_seqlens_q[b], cu_seqlens_q[b+1]) of q and o and key rows
+ * [cu_seqlens_k[b], cu_seqlens_k[b+1]) of k and v, and is an independent
+ * attention problem (bottom-right causal within it when causal != 0).
+ *   q, o   [total_q][n_q_heads][d] bf16, sequences back to back
+ *   k, v   [total_k][n_kv_heads][d] bf16 (may be NULL when total_k == 0)
+ *   lse    [n_q_heads][total_q] fp32 natural-log LSE, or NULL
+ *   cu_seqlens_q, cu_seqlens_k  int32[batch + 1] on the device, non-decreasing,
+ *          starting at 0; offsets are clamped to [0, total] on the device, so
+ *          inconsistent values cannot address outside the buffers.
+ *   max_seqlen_q  at least the longest query length: it sizes the grid, and
+ *          query rows past it are not computed.
+ * A sequence with no keys gets O = 0 and LSE = -inf. Requires d == 64 or
+ * d == 128 and total_q >= 1. Same kernel as attn_fwd, one work-group per
+ * (256-row query tile, sequence, query head), longest tile index first; a
+ * work-group past its sequence's last tile exits at once.
+ */
+int attn_fwd_varlen(const void *q, const void *k, const void *v, const int32_t *cu_seqlens_q,
+                    const int32_t *cu_seqlens_k, void *o, float *lse, int causal, int batch,
+                    int max_seqlen_q, int total_q, int total_k, int n_q_heads, int n_kv_heads, int d,
+                    void *stream);
+
+/* attn_fwd_varlen for IEEE fp16 q, k, v and o (same layouts and errors). */
+int attn_fwd_varlen_f16(const void *q, const void *k, const void *v, const int32_t *cu_seqlens_q,
+                        const int32_t *cu_seqlens_k, void *o, float *lse, int causal, int batch,
+                        int max_seqlen_q, int total_q, int total_k, int n_q_heads, int n_kv_heads,
+                        int d, void *stream);
+
+/*
  * Bytes of workspace attn_bwd needs: 2 * batch * n_q_heads * Sq_pad * 4 with
  * Sq_pad = seqlen_q rounded up to a multiple of 128 (a base-2 LSE and the row
  * sum D per query row). No initialisation is needed. Returns 0 for invalid

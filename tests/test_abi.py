@@ -139,3 +139,20 @@ def test_backward_validation_before_any_device_work():
     assert call(dk=odd) == aa.ATTN_ERR_MISALIGNED and call(lse=ctypes.c_void_p(0x1001)) == aa.ATTN_ERR_MISALIGNED
     assert call(wsb=ws_ok - 4) == aa.ATTN_ERR_WORKSPACE
     assert call(fn=L.attn_bwd_f16, d=80) == aa.ATTN_ERR_UNSUPPORTED
+
+
+def test_varlen_validation_before_any_device_work():
+    L = ensure_built()
+    f, odd = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x1002)
+
+    def call(q=f, k=f, v=f, cq=f, ck=f, o=f, lse=None, causal=1, B=2, mq=16, tq=20, tk=20, Hq=8, Hkv=8, d=64,
+             fn=L.attn_fwd_varlen):
+        return fn(q, k, v, cq, ck, o, lse, causal, B, mq, tq, tk, Hq, Hkv, d, None)
+
+    for name in ("q", "cq", "ck", "o"):
+        assert call(**{name: None}) == aa.ATTN_ERR_INVALID, name
+    assert call(k=None) == aa.ATTN_ERR_INVALID            # keys present but no k
+    assert call(B=0) == aa.ATTN_ERR_INVALID and call(mq=0) == aa.ATTN_ERR_INVALID and call(tq=0) == aa.ATTN_ERR_INVALID
+    assert call(Hkv=3) == aa.ATTN_ERR_INVALID and call(d=32) == aa.ATTN_ERR_UNSUPPORTED
+    assert call(cq=ctypes.c_void_p(0x1001)) == aa.ATTN_ERR_MISALIGNED and call(o=odd) == aa.ATTN_ERR_MISALIGNED
+    assert call(fn=L.attn_fwd_varlen_f16, d=96) == aa.ATTN_ERR_UNSUPPORTED
