@@ -7,14 +7,16 @@ A step is one pass of the whole path over one batch of synthetic input:
     kernel + combine, through the C ABI;
   * causal prefill (batch 2, 32 heads, d = 128, S = 8192) through attn_fwd;
   * the backward pass of that prefill (dQ, dK, dV from its O and LSE and a
-    synthetic dO) through attn_bwd.
+    synthetic dO) through attn_bwd;
+  * a packed variable-length causal prefill (16 sequences, lengths uniform in
+    [256, 4096], 32 heads, d = 128) through attn_fwd_varlen.
 The headline `value` is decode KV-read bandwidth: algorithmic K+V bytes
 (sum_b L_b * Hkv * 4d) over the measured duration of the decode call, timed
 with HIP events on the stream the kernels run on. Prefill TFLOP/s (exact causal
 FLOPs, 4 d per visible query-key pair) is reported beside it, and backward
 TFLOP/s counted, as the backward page does, as 2.5 times the forward FLOPs.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-backward]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-backward] [--no-varlen]
 Prints one JSON line.
 
 HBM traffic (roofline.traffic) comes from two rocprofv3 counter passes over
@@ -170,6 +172,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-varlen", action="store_true")
     ap.add_argument("--counter-run", action="store_true",
                     help="one copy, one decode and one prefill dispatch for rocprofv3 --pmc passes")
     ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
@@ -237,6 +240,18 @@ def main():
         del xp
     else:
         run_backward = False
+    run_varlen = not args.no_varlen
+    if run_varlen:
+        xv = wl.varlen_prefill_inputs()
+        lens_v = np.diff(xv.cu_q).astype(np.int64)
+        qv, kv_, vv = to_dev(xv.q), to_dev(xv.k), to_dev(xv.v)
+        cqv = torch.from_numpy(xv.cu_q.copy()).to(dev)
+        ckv = torch.from_numpy(xv.cu_k.copy()).to(dev)
+        ov = torch.empty_like(qv)
+        lsev = torch.empty((qv.shape[1], qv.shape[0]), dtype=torch.float32, device=dev)
+        max_qv = int(lens_v.max())
+        varlen_name = xv.meta["config"]
+        del xv
     setup_s = time.perf_counter() - t0
 
     stream = torch.cuda.current_stream()
@@ -272,11 +287,15 @@ def main():
             aa.attn_bwd(qp, kp, vp, op, lsep, dop, dqp, dkp, dvp, wsb, causal=True, stream=stream)
         if evs:
             evs[3].record(stream)
+        if run_varlen:
+            aa.attn_fwd_varlen(qv, kv_, vv, cqv, ckv, ov, max_qv, lse=lsev, causal=True, stream=stream)
+        if evs:
+            evs[4].record(stream)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(args.steps):
@@ -286,6 +305,7 @@ def main():
     dec_ms = [e[0].elapsed_time(e[1]) for e in events]
     pre_ms = [e[1].elapsed_time(e[2]) for e in events]
     bwd_ms = [e[2].elapsed_time(e[3]) for e in events]
+    var_ms = [e[3].elapsed_time(e[4]) for e in events]
     dec_mean = statistics.fmean(dec_ms)
     pre_mean = statistics.fmean(pre_ms) if run_prefill else 0.0
 
@@ -329,6 +349,7 @@ def main():
             "pieces_per_kv_head": pieces,
             "prefill_workload": "causal-prefill b=2 h=32 d=128 s=8192 (seed 1004)" if run_prefill else None,
             "backward_workload": "backward of that prefill, dO seed 1005" if run_backward else None,
+            "varlen_workload": varlen_name if run_varlen else None,
             "parallelism": "single-gpu",
             "device": props.name,
             "cus": props.multi_processor_count,
@@ -387,6 +408,23 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(tf / BF16_PEAK_TFLOPS, 4),
             "traffic": measured_traffic("attn_bwd", source_hash(BWD_SOURCES), None),
+        }
+    if run_varlen:
+        var_mean = statistics.fmean(var_ms)
+        Hv, dv_ = qv.shape[1], qv.shape[2]
+        fl = int(sum(4 * dv_ * Hv * (int(L) * (int(L) + 1) // 2) for L in lens_v))  # exact causal FLOPs
+        tf = fl / (var_mean * 1e-3) / 1e12
+        result["varlen_prefill"] = {
+            "bound": "mfma",
+            "kernel": "fwd_pp (packed offsets)",
+            "ms_mean": round(var_mean, 5),
+            "ms_median": round(statistics.median(var_ms), 5),
+            "tokens": int(lens_v.sum()),
+            "flops": fl,
+            "achieved": round(tf, 2),
+            "peak": BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tf / BF16_PEAK_TFLOPS, 4),
         }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline_decode(xd, d)

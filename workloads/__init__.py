@@ -223,6 +223,16 @@ def make_varlen(lens_q, lens_k, n_q_heads, n_kv_heads, d, seed, dtype="bf16") ->
     return VarlenInputs(q, k, v, cu_q, cu_k, dict(seed=seed), dtype)
 
 
+def varlen_prefill_inputs(seed: int = 1006, batch: int = 16, lo: int = 256, hi: int = 4096,
+                          n_heads: int = 32, d: int = 128) -> VarlenInputs:
+    """Variable-length causal prefill: `batch` sequences with query = key lengths
+    uniform in [lo, hi] (stream TID_LEN), MHA, packed."""
+    lens = draw_lengths(seed, batch, lo, hi)
+    out = make_varlen(lens, lens, n_heads, n_heads, d, seed)
+    out.meta["config"] = f"varlen-prefill b={batch} h={n_heads} d={d} len~U[{lo},{hi}] (seed {seed})"
+    return out
+
+
 def make_grad_out(q: np.ndarray, seed: int, dtype: str = "bf16") -> np.ndarray:
     """Output gradient dO shaped like q: N(0,1) draws of stream (seed, TID_DO)."""
     return normal_bits(seed, TID_DO, q.size, dtype=dtype).reshape(q.shape)
