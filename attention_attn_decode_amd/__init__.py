@@ -28,7 +28,8 @@ ATTN_MAX_BATCH = 8192
 # Every symbol include/attn.h declares.
 EXPORTS = ("attn_decode_plan", "attn_decode_workspace_size", "attn_decode", "attn_decode_ex",
            "attn_decode_f16", "attn_fwd", "attn_fwd_f16", "attn_fwd_varlen", "attn_fwd_varlen_f16",
-           "attn_bwd_workspace_size", "attn_bwd",
+           "attn_bwd_workspace_size", "attn_bwd", "attn_bwd_varlen_workspace_size", "attn_bwd_varlen",
+           "attn_bwd_varlen_f16",
            "attn_bwd_f16", "attn_status_string", "attn_version")
 
 _lib = None
@@ -71,6 +72,11 @@ def lib() -> ctypes.CDLL:
     for name in ("attn_bwd", "attn_bwd_f16"):
         getattr(L, name).argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, sz,
                                      vp]
+        getattr(L, name).restype = i32
+    L.attn_bwd_varlen_workspace_size.argtypes = [i32, i32]
+    L.attn_bwd_varlen_workspace_size.restype = sz
+    for name in ("attn_bwd_varlen", "attn_bwd_varlen_f16"):
+        getattr(L, name).argtypes = [vp] * 11 + [i32] * 9 + [vp, sz, vp]
         getattr(L, name).restype = i32
     L.attn_status_string.argtypes = [i32]
     L.attn_status_string.restype = ctypes.c_char_p
@@ -263,3 +269,43 @@ def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, causal=True, stream=N
             1 if causal else 0, B, Sq, Sk, Hq, Hkv, d, _ptr(workspace), wbytes, _stream_ptr(stream))
     if st != ATTN_OK:
         raise AttnError(st, "attn_bwd")
+
+
+def attn_bwd_varlen_workspace_size(n_q_heads, total_q) -> int:
+    """Bytes of workspace attn_bwd_varlen needs (uninitialised memory is fine)."""
+    return int(lib().attn_bwd_varlen_workspace_size(n_q_heads, total_q))
+
+
+def attn_bwd_varlen(q, k, v, o, lse, dout, dq, dk, dv, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                    workspace, causal=True, stream=None):
+    """Backward over a packed variable-length batch. q, o, dout, dq: [total_q, Hq, d]; k, v, dk, dv:
+    [total_k, Hkv, d] (bf16 or fp16); lse fp32 [Hq, total_q]; cu_seqlens_q/k int32 [B + 1]."""
+    import torch
+    et, f16 = _elem(q)
+    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout"), (dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _check(t, nm, et, 3)
+    _check(lse, "lse", torch.float32, 2)
+    _check(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1)
+    _check(cu_seqlens_k, "cu_seqlens_k", torch.int32, 1)
+    tq, Hq, d = q.shape
+    tk, Hkv, dk_ = k.shape
+    B = cu_seqlens_q.shape[0] - 1
+    if tuple(v.shape) != tuple(k.shape) or dk_ != d or cu_seqlens_k.shape[0] != B + 1 or B < 1:
+        raise ValueError("k, v must be [total_k, Hkv, d] and both offset arrays B + 1 long")
+    for t, nm in ((o, "o"), (dout, "dout"), (dq, "dq")):
+        if tuple(t.shape) != tuple(q.shape):
+            raise ValueError(f"{nm} must match q")
+    for t, nm in ((dk, "dk"), (dv, "dv")):
+        if tuple(t.shape) != tuple(k.shape):
+            raise ValueError(f"{nm} must match k")
+    if tuple(lse.shape) != (Hq, tq):
+        raise ValueError("lse must be [Hq, total_q]")
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous device memory")
+    wbytes = workspace.numel() * workspace.element_size()
+    fn = lib().attn_bwd_varlen_f16 if f16 else lib().attn_bwd_varlen
+    st = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+            _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), 1 if causal else 0, B, int(max_seqlen_q), int(max_seqlen_k),
+            tq, tk, Hq, Hkv, d, _ptr(workspace), wbytes, _stream_ptr(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_bwd_varlen")

@@ -18,9 +18,11 @@ hipError_t launch_fwd(const void *q, const void *k, const void *v, void *o, floa
                       const int *cu_k, int total_q, int total_k, int causal, int batch, int Sq, int Sk, int Hq,
                       int Hkv, int d, float scale_log2, bool f16, hipStream_t stream);
 hipError_t launch_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse, const void *dout,
-                      void *dq, void *dk, void *dv, int causal, int batch, int Sq, int Sk, int Hq, int Hkv, int d,
-                      float *l2ws, float *dws, bool f16, hipStream_t stream);
+                      void *dq, void *dk, void *dv, const int *cu_q, const int *cu_k, int total_q, int total_k,
+                      int causal, int batch, int Sq, int Sk, int Hq, int Hkv, int d, float *l2ws, float *dws, bool f16,
+                      hipStream_t stream);
 int bwd_sq_pad(int Sq);
+int bwd_varlen_pad(int total_q);
 }  // namespace attn
 
 namespace {
@@ -183,8 +185,43 @@ int bwd_impl(const void *q, const void *k, const void *v, const void *o, const f
   float *l2ws = static_cast<float *>(workspace);
   float *dws = l2ws + rows;
   const hipError_t err =
-      attn::launch_bwd(q, k, v, o, lse, dout, dq, dk, dv, causal ? 1 : 0, batch, seqlen_q, seqlen_k, n_q_heads,
-                       n_kv_heads, d, l2ws, dws, f16, static_cast<hipStream_t>(stream));
+      attn::launch_bwd(q, k, v, o, lse, dout, dq, dk, dv, nullptr, nullptr, 0, 0, causal ? 1 : 0, batch, seqlen_q,
+                       seqlen_k, n_q_heads, n_kv_heads, d, l2ws, dws, f16, static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+size_t bwd_varlen_workspace(int n_q_heads, int total_q) {
+  return 2 * (size_t)n_q_heads * (size_t)attn::bwd_varlen_pad(total_q) * sizeof(float);
+}
+
+int bwd_varlen_impl(const void *q, const void *k, const void *v, const void *o, const float *lse, const void *dout,
+                    void *dq, void *dk, void *dv, const int32_t *cu_q, const int32_t *cu_k, int causal, int batch,
+                    int max_seqlen_q, int max_seqlen_k, int total_q, int total_k, int n_q_heads, int n_kv_heads, int d,
+                    void *workspace, size_t workspace_bytes, void *stream, bool f16) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !cu_q || !cu_k || !workspace)
+    return ATTN_ERR_INVALID;
+  if (batch <= 0 || max_seqlen_q <= 0 || max_seqlen_k <= 0 || total_q <= 0 || total_k <= 0 || n_q_heads <= 0 ||
+      n_kv_heads <= 0)
+    return ATTN_ERR_INVALID;
+  if (n_q_heads % n_kv_heads != 0) return ATTN_ERR_INVALID;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  if (n_q_heads > 65535) return ATTN_ERR_UNSUPPORTED;
+  const long long qtiles = (long long)(max_seqlen_q + 127) / 128 * batch * n_q_heads;
+  const long long ktiles = (long long)(max_seqlen_k + 127) / 128 * batch * n_kv_heads;
+  const long long rows = (long long)attn::bwd_varlen_pad(total_q) * n_q_heads;
+  if (qtiles > 0x7fffffffLL || ktiles > 0x7fffffffLL || rows > 0x3fffffffLL || total_q > 0x3fffff00)
+    return ATTN_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(dq) ||
+      !aligned16(dk) || !aligned16(dv) || !aligned4(lse) || !aligned4(cu_q) || !aligned4(cu_k) ||
+      !aligned16(workspace))
+    return ATTN_ERR_MISALIGNED;
+  if (workspace_bytes < bwd_varlen_workspace(n_q_heads, total_q)) return ATTN_ERR_WORKSPACE;
+  float *l2ws = static_cast<float *>(workspace);
+  float *dws = l2ws + rows;
+  const hipError_t err =
+      attn::launch_bwd(q, k, v, o, lse, dout, dq, dk, dv, cu_q, cu_k, total_q, total_k, causal ? 1 : 0, batch,
+                       max_seqlen_q, max_seqlen_k, n_q_heads, n_kv_heads, d, l2ws, dws, f16,
+                       static_cast<hipStream_t>(stream));
   return err == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
@@ -209,6 +246,30 @@ int attn_bwd_f16(const void *q, const void *k, const void *v, const void *o, con
                  int n_kv_heads, int d, void *workspace, size_t workspace_bytes, void *stream) {
   return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, causal, batch, seqlen_q, seqlen_k, n_q_heads, n_kv_heads, d,
                   workspace, workspace_bytes, stream, true);
+}
+
+size_t attn_bwd_varlen_workspace_size(int n_q_heads, int total_q) {
+  if (n_q_heads <= 0 || total_q <= 0) return 0;
+  return bwd_varlen_workspace(n_q_heads, total_q);
+}
+
+int attn_bwd_varlen(const void *q, const void *k, const void *v, const void *o, const float *lse, const void *dout,
+                    void *dq, void *dk, void *dv, const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k, int causal,
+                    int batch, int max_seqlen_q, int max_seqlen_k, int total_q, int total_k, int n_q_heads,
+                    int n_kv_heads, int d, void *workspace, size_t workspace_bytes, void *stream) {
+  return bwd_varlen_impl(q, k, v, o, lse, dout, dq, dk, dv, cu_seqlens_q, cu_seqlens_k, causal, batch, max_seqlen_q,
+                         max_seqlen_k, total_q, total_k, n_q_heads, n_kv_heads, d, workspace, workspace_bytes, stream,
+                         false);
+}
+
+int attn_bwd_varlen_f16(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                        const void *dout, void *dq, void *dk, void *dv, const int32_t *cu_seqlens_q,
+                        const int32_t *cu_seqlens_k, int causal, int batch, int max_seqlen_q, int max_seqlen_k,
+                        int total_q, int total_k, int n_q_heads, int n_kv_heads, int d, void *workspace,
+                        size_t workspace_bytes, void *stream) {
+  return bwd_varlen_impl(q, k, v, o, lse, dout, dq, dk, dv, cu_seqlens_q, cu_seqlens_k, causal, batch, max_seqlen_q,
+                         max_seqlen_k, total_q, total_k, n_q_heads, n_kv_heads, d, workspace, workspace_bytes, stream,
+                         true);
 }
 
 int attn_decode_ex(const void *q, const void *k_cache, const void *v_cache,

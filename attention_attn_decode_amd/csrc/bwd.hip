@@ -151,7 +151,8 @@ template <int D, bool F16>
 __global__ void __launch_bounds__(256, 2)
 bwd_dkdv(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
          const uint16_t *__restrict__ dout, const float *__restrict__ l2ws, const float *__restrict__ dws,
-         uint16_t *__restrict__ dk, uint16_t *__restrict__ dv, int Sq, int Sq_pad, int Sk, int Hq, int Hkv,
+         uint16_t *__restrict__ dk, uint16_t *__restrict__ dv, const int *__restrict__ cu_q,
+         const int *__restrict__ cu_k, int total_q, int total_k, int Sq, int Sq_pad, int Sk, int Hq, int Hkv,
          int causal, float scale_log2, float scale, int BHkv) {
   constexpr int KST = D / 16, MT = D / 32, CH = D / 8;
   constexpr int QT = kQB * D;                 // one Q (or dO) tile, elements
@@ -166,6 +167,19 @@ bwd_dkdv(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const u
   const int u = x % BHkv;
   const int b = u / Hkv, g = u % Hkv;
   const int G = Hq / Hkv;
+  // Rows of sequence b (dense [B][S] blocks, or packed offsets clamped to the
+  // totals) and its row statistics in the workspace: [B][Hq][Sq_pad] dense,
+  // [Hq][Sq_pad] over the packed rows.
+  int qbase, kbase;
+  size_t stat_b;
+  if (cu_q != nullptr) {
+    const int a0 = min(max(cu_q[b], 0), total_q), a1 = min(max(cu_q[b + 1], a0), total_q);
+    const int c0 = min(max(cu_k[b], 0), total_k), c1 = min(max(cu_k[b + 1], c0), total_k);
+    qbase = a0, Sq = a1 - a0, kbase = c0, Sk = c1 - c0, stat_b = (size_t)a0;
+    if (kt * kKT >= Sk) return;  // the whole work-group: this sequence has fewer key tiles
+  } else {
+    qbase = b * Sq, kbase = b * Sk, stat_b = (size_t)b * Hq * Sq_pad;
+  }
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, hl = lane >> 5;
   const int k0 = kt * kKT, kw0 = k0 + 32 * w;  // first key of the tile, of the wave
@@ -175,7 +189,7 @@ bwd_dkdv(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const u
   // This lane's K and V row as B operands (d contracted), zero past Sk.
   uint4 kop[KST], vop[kVinLds ? 1 : KST];
   {
-    const size_t roff = ((size_t)((size_t)b * Sk + (key < Sk ? key : 0)) * Hkv + g) * D;
+    const size_t roff = ((size_t)((size_t)kbase + (key < Sk ? key : 0)) * Hkv + g) * D;
 #pragma unroll
     for (int kk = 0; kk < KST; ++kk) {
       const bool ok = key < Sk;
@@ -185,7 +199,7 @@ bwd_dkdv(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const u
     if constexpr (kVinLds) {
       // The work-group's 128 V rows, swizzled like the streamed tiles; read
       // row-wise (16 consecutive rows per chunk) as the dP operand.
-      const size_t vbase = ((size_t)b * Sk * Hkv + g) * D;
+      const size_t vbase = ((size_t)kbase * Hkv + g) * D;
       for (int c = tid; c < kKT * CH; c += 256) {
         const int r = c / CH, ch = c % CH, kr = k0 + r;
         const uint4 val = kr < Sk ? ldg16(v + vbase + (size_t)kr * Hkv * D + ch * 8) : make_uint4(0, 0, 0, 0);
@@ -208,14 +222,12 @@ bwd_dkdv(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const u
   const size_t rstride = (size_t)Hq * D;
   const int tg = tid, trow = tg / CH, tch = tg % CH;
   uint4 sq[LPT], sdo[LPT];
-  float4 sst;  // threads 0-15: four L2 (0-7) or D (8-15) values of the step's rows
+  float sst;  // threads 0-63: the L2 (0-31) or D (32-63) value of one of the step's rows
   auto load_step = [&](int st) {
     const int hh = st / (nqb - ib0), ib = ib0 + st % (nqb - ib0);
     const int h = g * G + hh;
-    if (tid < 16)
-      sst = *reinterpret_cast<const float4 *>((tid < 8 ? l2ws : dws) + ((size_t)b * Hq + h) * Sq_pad + ib * kQB +
-                                              4 * (tid & 7));
-    const long long base = ((long long)b * Sq * Hq + h) * D + (long long)ib * kQB * rstride;
+    if (tid < 64) sst = (tid < 32 ? l2ws : dws)[stat_b + (size_t)h * Sq_pad + ib * kQB + (tid & 31)];
+    const long long base = ((long long)qbase * Hq + h) * D + (long long)ib * kQB * rstride;
     const long long left = ((long long)Sq * Hq - h) * D * 2 - (long long)ib * kQB * rstride * 2;
     const auto rq = buffer_rsrc(q + base, left), rd = buffer_rsrc(dout + base, left);
 #pragma unroll
@@ -233,7 +245,7 @@ bwd_dkdv(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const u
       sts16(qt + tile_off<D>(r, tch), sq[i]);
       sts16(dt + tile_off<D>(r, tch), sdo[i]);
     }
-    if (tid < 16) *reinterpret_cast<float4 *>(&stat[slot][tid >> 3][4 * (tid & 7)]) = sst;
+    if (tid < 64) stat[slot][tid >> 5][tid & 31] = sst;
   };
 
   if (nsteps > 0) {
@@ -341,7 +353,7 @@ bwd_dkdv(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const u
   }
 
   if (key >= Sk) return;
-  const size_t ooff = ((size_t)((size_t)b * Sk + key) * Hkv + g) * D;
+  const size_t ooff = ((size_t)((size_t)kbase + key) * Hkv + g) * D;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -365,8 +377,9 @@ template <int D, bool F16>
 __global__ void __launch_bounds__(256, 2)
 bwd_dq(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
        const uint16_t *__restrict__ dout, const float *__restrict__ l2ws, const float *__restrict__ dws,
-       uint16_t *__restrict__ dq, int Sq, int Sq_pad, int Sk, int Hq, int Hkv, int causal, float scale_log2,
-       float scale, int n_qtiles, int BH) {
+       uint16_t *__restrict__ dq, const int *__restrict__ cu_q, const int *__restrict__ cu_k, int total_q,
+       int total_k, int Sq, int Sq_pad, int Sk, int Hq, int Hkv, int causal, float scale_log2, float scale,
+       int n_qtiles, int BH) {
   constexpr int KST = D / 16, MT = D / 32, CH = D / 8;
   constexpr int KTL = kKB * D;          // one K (or V) tile, elements
   constexpr int LPT = kKB * CH / 256;   // 16-byte chunks per thread per tile
@@ -381,20 +394,32 @@ bwd_dq(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uin
   const int n = lane & 31, hl = lane >> 5;
   const int q0 = qt_ * kQT, r0 = q0 + 32 * w;
   const int qrow = r0 + n;
+  int qbase, kbase;  // as in bwd_dkdv
+  size_t stat_b;
+  if (cu_q != nullptr) {
+    const int a0 = min(max(cu_q[b], 0), total_q), a1 = min(max(cu_q[b + 1], a0), total_q);
+    const int c0 = min(max(cu_k[b], 0), total_k), c1 = min(max(cu_k[b + 1], c0), total_k);
+    qbase = a0, Sq = a1 - a0, kbase = c0, Sk = c1 - c0, stat_b = (size_t)a0;
+    if (q0 >= Sq) return;  // the whole work-group: this sequence has fewer query tiles
+  } else {
+    qbase = b * Sq, kbase = b * Sk, stat_b = (size_t)b * Hq * Sq_pad;
+  }
   const int off = Sk - Sq;
 
   uint4 qop[KST], doop[KST];
   {
     const bool ok = qrow < Sq;
-    const size_t roff = ((size_t)((size_t)b * Sq + (ok ? qrow : 0)) * Hq + h) * D;
+    const size_t roff = ((size_t)((size_t)qbase + (ok ? qrow : 0)) * Hq + h) * D;
 #pragma unroll
     for (int kk = 0; kk < KST; ++kk) {
       qop[kk] = ok ? ldg16(q + roff + (2 * kk + hl) * 8) : make_uint4(0, 0, 0, 0);
       doop[kk] = ok ? ldg16(dout + roff + (2 * kk + hl) * 8) : make_uint4(0, 0, 0, 0);
     }
   }
-  const float l2 = l2ws[((size_t)b * Hq + h) * Sq_pad + qrow];  // qrow < Sq_pad: padded rows hold +inf
-  const float Dr = dws[((size_t)b * Hq + h) * Sq_pad + qrow];
+  // In range for every row of the tile (the padding covers a full tile past
+  // the last row); a row past Sq is masked whatever value it reads.
+  const float l2 = l2ws[stat_b + (size_t)h * Sq_pad + qrow];
+  const float Dr = dws[stat_b + (size_t)h * Sq_pad + qrow];
   f32x16 dqT[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
@@ -412,7 +437,7 @@ bwd_dq(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uin
   const int trow = tid / CH, tch = tid % CH;
   uint4 sk[LPT], sv[LPT];
   auto load_blk = [&](int blk) {
-    const long long base = ((long long)b * Sk * Hkv + gk) * D + (long long)blk * kKB * rstride;
+    const long long base = ((long long)kbase * Hkv + gk) * D + (long long)blk * kKB * rstride;
     const long long left = ((long long)Sk * Hkv - gk) * D * 2 - (long long)blk * kKB * rstride * 2;
     const auto rk = buffer_rsrc(k + base, left), rv = buffer_rsrc(v + base, left);
 #pragma unroll
@@ -500,7 +525,7 @@ bwd_dq(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uin
   }
 
   if (qrow >= Sq) return;
-  uint16_t *dst = dq + ((size_t)((size_t)b * Sq + qrow) * Hq + h) * D;
+  uint16_t *dst = dq + ((size_t)((size_t)qbase + qrow) * Hq + h) * D;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -515,37 +540,48 @@ bwd_dq(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uin
 }  // namespace
 
 int bwd_sq_pad(int Sq) { return (Sq + kQT - 1) / kQT * kQT; }
+// Packed batches: one [Hq][pad] statistics block over all rows, padded by a
+// full query tile past the last row (a tile's reads may start at any row).
+int bwd_varlen_pad(int total_q) { return (total_q + kQT + kQT - 1) / kQT * kQT; }
 
+// Dense when cu_q == nullptr: Sq, Sk are the per-sequence lengths. Packed
+// otherwise: Sq, Sk are the longest lengths (they size the grids) and
+// total_q, total_k the packed row counts.
 hipError_t launch_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse, const void *dout,
-                      void *dq, void *dk, void *dv, int causal, int batch, int Sq, int Sk, int Hq, int Hkv, int d,
-                      float *l2ws, float *dws, bool f16, hipStream_t stream) {
+                      void *dq, void *dk, void *dv, const int *cu_q, const int *cu_k, int total_q, int total_k,
+                      int causal, int batch, int Sq, int Sk, int Hq, int Hkv, int d, float *l2ws, float *dws, bool f16,
+                      hipStream_t stream) {
   const auto *qq = static_cast<const uint16_t *>(q);
   const auto *kk = static_cast<const uint16_t *>(k);
   const auto *vv = static_cast<const uint16_t *>(v);
   const auto *oo = static_cast<const uint16_t *>(o);
   const auto *gg = static_cast<const uint16_t *>(dout);
-  const int Sq_pad = bwd_sq_pad(Sq);
+  const bool packed = cu_q != nullptr;
+  const int Sq_pad = packed ? bwd_varlen_pad(total_q) : bwd_sq_pad(Sq);
   const float scale = 1.f / sqrtf((float)d), scale_log2 = scale * kLog2e;
   {
-    const long long rows = (long long)batch * Hq * Sq_pad;
+    // Row statistics: a packed batch is one sequence of total_q rows here.
+    const int pb = packed ? 1 : batch, psq = packed ? total_q : Sq;
+    const long long rows = (long long)pb * Hq * Sq_pad;
     const int rows_per_block = 256 / (d / 8);
     const long long blocks = (rows + rows_per_block - 1) / rows_per_block;
     const dim3 grid((unsigned)(blocks < 65536 ? blocks : 65536));
     if (d == 128)
-      hipLaunchKernelGGL(bwd_pre<128>, grid, dim3(256), 0, stream, oo, gg, lse, l2ws, dws, batch, Sq, Sq_pad, Hq, f16);
+      hipLaunchKernelGGL(bwd_pre<128>, grid, dim3(256), 0, stream, oo, gg, lse, l2ws, dws, pb, psq, Sq_pad, Hq, f16);
     else
-      hipLaunchKernelGGL(bwd_pre<64>, grid, dim3(256), 0, stream, oo, gg, lse, l2ws, dws, batch, Sq, Sq_pad, Hq, f16);
+      hipLaunchKernelGGL(bwd_pre<64>, grid, dim3(256), 0, stream, oo, gg, lse, l2ws, dws, pb, psq, Sq_pad, Hq, f16);
   }
   const int BHkv = batch * Hkv, BH = batch * Hq;
   const int n_ktiles = (Sk + kKT - 1) / kKT, n_qtiles = (Sq + kQT - 1) / kQT;
   auto dkdv = [&](auto kern) {
     hipLaunchKernelGGL(kern, dim3(n_ktiles * BHkv), dim3(256), 0, stream, qq, kk, vv, gg, l2ws, dws,
-                       static_cast<uint16_t *>(dk), static_cast<uint16_t *>(dv), Sq, Sq_pad, Sk, Hq, Hkv, causal,
-                       scale_log2, scale, BHkv);
+                       static_cast<uint16_t *>(dk), static_cast<uint16_t *>(dv), cu_q, cu_k, total_q, total_k, Sq,
+                       Sq_pad, Sk, Hq, Hkv, causal, scale_log2, scale, BHkv);
   };
   auto dqk = [&](auto kern) {
     hipLaunchKernelGGL(kern, dim3(n_qtiles * BH), dim3(256), 0, stream, qq, kk, vv, gg, l2ws, dws,
-                       static_cast<uint16_t *>(dq), Sq, Sq_pad, Sk, Hq, Hkv, causal, scale_log2, scale, n_qtiles, BH);
+                       static_cast<uint16_t *>(dq), cu_q, cu_k, total_q, total_k, Sq, Sq_pad, Sk, Hq, Hkv, causal,
+                       scale_log2, scale, n_qtiles, BH);
   };
   if (d == 128) {
     if (f16) dkdv(bwd_dkdv<128, true>), dqk(bwd_dq<128, true>);

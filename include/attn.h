@@ -242,6 +242,36 @@ int attn_bwd_f16(const void *q, const void *k, const void *v, const void *o, con
                  int seqlen_k, int n_q_heads, int n_kv_heads, int d, void *workspace,
                  size_t workspace_bytes, void *stream);
 
+/*
+ * Bytes of workspace attn_bwd_varlen needs: 2 * n_q_heads * pad * 4 with
+ * pad = total_q + 128 rounded up to a multiple of 128. Returns 0 for invalid
+ * arguments. Host-only.
+ */
+size_t attn_bwd_varlen_workspace_size(int n_q_heads, int total_q);
+
+/*
+ * attn_bwd over a packed variable-length batch (the layouts, offsets and
+ * clamping of attn_fwd_varlen): q, o, dout, dq [total_q][n_q_heads][d];
+ * k, v, dk, dv [total_k][n_kv_heads][d]; lse [n_q_heads][total_q], the
+ * forward's. max_seqlen_q and max_seqlen_k are at least the longest query
+ * and key lengths (they size the grids). Each sequence is an independent
+ * problem; dq, dk and dv are written exactly once per row of a sequence.
+ * Requires total_q >= 1, total_k >= 1 and a workspace of
+ * attn_bwd_varlen_workspace_size() bytes.
+ */
+int attn_bwd_varlen(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                    const void *dout, void *dq, void *dk, void *dv, const int32_t *cu_seqlens_q,
+                    const int32_t *cu_seqlens_k, int causal, int batch, int max_seqlen_q,
+                    int max_seqlen_k, int total_q, int total_k, int n_q_heads, int n_kv_heads, int d,
+                    void *workspace, size_t workspace_bytes, void *stream);
+
+/* attn_bwd_varlen for IEEE fp16 tensors (same layouts, workspace and errors). */
+int attn_bwd_varlen_f16(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                        const void *dout, void *dq, void *dk, void *dv, const int32_t *cu_seqlens_q,
+                        const int32_t *cu_seqlens_k, int causal, int batch, int max_seqlen_q,
+                        int max_seqlen_k, int total_q, int total_k, int n_q_heads, int n_kv_heads,
+                        int d, void *workspace, size_t workspace_bytes, void *stream);
+
 /* Static description of a status code; never NULL. */
 const char *attn_status_string(int status);
 

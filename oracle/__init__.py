@@ -26,5 +26,12 @@ from .attention import (  # noqa: F401
     combine_partials,
     decode_row_counts,
 )
-from .backward import attention_backward, backward_error_scales, backward_f64, backward_kv_head  # noqa: F401
+from .backward import (  # noqa: F401
+    attention_backward,
+    attention_backward_varlen,
+    backward_error_scales,
+    backward_error_scales_varlen,
+    backward_f64,
+    backward_kv_head,
+)
 from .brute import brute_attention  # noqa: F401

@@ -145,3 +145,28 @@ def backward_error_scales(q, k, v, do, causal=True, dtype="bf16", row_block=512)
                 ek[b, :, g] += scale * (a.T @ np.abs(qq))
                 eq[b, i0:i1, h] = scale * (a @ np.abs(kk))
     return eq, ek, ev
+
+
+def _varlen_apply(fn, q, k, v, do, cu_q, cu_k, causal, dtype):
+    """Run a per-batch backward function on each sequence of a packed batch; pack the results."""
+    tq, Hq, d = q.shape
+    tk, Hkv = k.shape[0], k.shape[1]
+    out_q, out_k, out_v = np.zeros((tq, Hq, d)), np.zeros((tk, Hkv, d)), np.zeros((tk, Hkv, d))
+    for b in range(len(cu_q) - 1):
+        s0, s1, t0, t1 = int(cu_q[b]), int(cu_q[b + 1]), int(cu_k[b]), int(cu_k[b + 1])
+        if s1 <= s0 or t1 <= t0:
+            continue
+        r = fn(q[None, s0:s1], k[None, t0:t1], v[None, t0:t1], do[None, s0:s1], causal, dtype=dtype)
+        out_q[s0:s1], out_k[t0:t1], out_v[t0:t1] = r[0][0], r[1][0], r[2][0]
+    return out_q, out_k, out_v
+
+
+def attention_backward_varlen(q, k, v, do, cu_q, cu_k, causal=True, dtype="bf16"):
+    """dq [total_q, Hq, d], dk and dv [total_k, Hkv, d] of a packed variable-length batch
+    (uint16 element patterns in, fp64 out): each sequence is an independent problem."""
+    return _varlen_apply(attention_backward, q, k, v, do, cu_q, cu_k, causal, dtype)
+
+
+def backward_error_scales_varlen(q, k, v, do, cu_q, cu_k, causal=True, dtype="bf16"):
+    """backward_error_scales of each sequence of a packed batch, packed."""
+    return _varlen_apply(backward_error_scales, q, k, v, do, cu_q, cu_k, causal, dtype)

@@ -156,3 +156,23 @@ def test_varlen_validation_before_any_device_work():
     assert call(Hkv=3) == aa.ATTN_ERR_INVALID and call(d=32) == aa.ATTN_ERR_UNSUPPORTED
     assert call(cq=ctypes.c_void_p(0x1001)) == aa.ATTN_ERR_MISALIGNED and call(o=odd) == aa.ATTN_ERR_MISALIGNED
     assert call(fn=L.attn_fwd_varlen_f16, d=96) == aa.ATTN_ERR_UNSUPPORTED
+
+
+def test_backward_varlen_validation_and_workspace():
+    L = ensure_built()
+    f = ctypes.c_void_p(0x1000)
+    for Hq, tq in ((1, 1), (32, 35024), (8, 129)):
+        pad = -(-(tq + 128) // 128) * 128
+        assert aa.attn_bwd_varlen_workspace_size(Hq, tq) == 2 * Hq * pad * 4
+    assert aa.attn_bwd_varlen_workspace_size(0, 5) == 0
+    ws_ok = aa.attn_bwd_varlen_workspace_size(8, 20)
+
+    def call(cq=f, ck=f, B=2, mq=16, mk=16, tq=20, tk=20, Hq=8, Hkv=8, d=64, ws=f, wsb=ws_ok, fn=L.attn_bwd_varlen):
+        return fn(f, f, f, f, f, f, f, f, f, cq, ck, 1, B, mq, mk, tq, tk, Hq, Hkv, d, ws, wsb, None)
+
+    assert call(cq=None) == aa.ATTN_ERR_INVALID and call(ws=None) == aa.ATTN_ERR_INVALID
+    assert call(tk=0) == aa.ATTN_ERR_INVALID and call(mk=0) == aa.ATTN_ERR_INVALID
+    assert call(d=80) == aa.ATTN_ERR_UNSUPPORTED and call(Hkv=3) == aa.ATTN_ERR_INVALID
+    assert call(ck=ctypes.c_void_p(0x1002)) == aa.ATTN_ERR_MISALIGNED
+    assert call(wsb=ws_ok - 1) == aa.ATTN_ERR_WORKSPACE
+    assert call(fn=L.attn_bwd_varlen_f16, d=96) == aa.ATTN_ERR_UNSUPPORTED

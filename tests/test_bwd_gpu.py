@@ -156,3 +156,59 @@ def test_bwd_causal_prefill_workload_sampled(aa):
     lhs, rhs = dv.sum(axis=1), dof.sum(axis=1)
     tol = 2 * u * (np.abs(dof).sum(axis=1) + np.abs(dv).sum(axis=1))
     assert np.all(np.abs(lhs - rhs) <= tol)
+
+
+# --- packed variable-length batches -------------------------------------------
+
+def run_bwd_varlen(aa, x, do_bits, causal=True):
+    torch = G.torch()
+    tq, Hq, d = x.q.shape
+    q, k, v = G.dev_bf16(x.q, x.dtype), G.dev_bf16(x.k, x.dtype), G.dev_bf16(x.v, x.dtype)
+    do = G.dev_bf16(do_bits, x.dtype)
+    cq, ck = G.dev_i32(x.cu_q), G.dev_i32(x.cu_k)
+    mq, mk = int(np.diff(x.cu_q).max()), int(np.diff(x.cu_k).max())
+    o = G.nan_like_bf16(q.shape, x.dtype)
+    lse = G.nan_f32((Hq, tq))
+    aa.attn_fwd_varlen(q, k, v, cq, ck, o, mq, lse=lse, causal=causal)
+    dq, dk, dv = G.nan_like_bf16(q.shape, x.dtype), G.nan_like_bf16(k.shape, x.dtype), G.nan_like_bf16(k.shape, x.dtype)
+    ws = torch.full((aa.attn_bwd_varlen_workspace_size(Hq, tq) // 4,), float("nan"), dtype=torch.float32,
+                    device="cuda")
+    aa.attn_bwd_varlen(q, k, v, o, lse, do, dq, dk, dv, cq, ck, mq, mk, ws, causal=causal)
+    torch.cuda.synchronize()
+    return G.host_f64(dq), G.host_f64(dk), G.host_f64(dv)
+
+
+VARLEN_CASES = [
+    # lens_q, lens_k, Hq, Hkv, d, causal
+    ([200, 1, 513, 64, 300], [200, 1, 513, 64, 128], 4, 2, 128, True),
+    ([100, 257, 30], [900, 257, 31], 2, 2, 64, True),
+    ([77, 300, 5, 256], [77, 300, 5, 256], 4, 4, 64, False),
+    ([129, 40, 3], [129, 50, 7], 3, 1, 128, False),
+    ([129, 0, 40, 70], [129, 50, 0, 70], 2, 2, 128, True),   # a sequence without queries, one without keys
+]
+
+
+@pytest.mark.parametrize("case", VARLEN_CASES)
+def test_bwd_varlen_against_oracle(aa, case):
+    lq, lk, Hq, Hkv, d, causal = case
+    x = wl.make_varlen(lq, lk, Hq, Hkv, d, seed=801 + sum(lq))
+    do = wl.make_grad_out(x.q, 802 + sum(lk))
+    dq, dk, dv = run_bwd_varlen(aa, x, do, causal)
+    rq, rk, rv = oracle.attention_backward_varlen(x.q, x.k, x.v, do, x.cu_q, x.cu_k, causal)
+    eq, ek, ev = oracle.backward_error_scales_varlen(x.q, x.k, x.v, do, x.cu_q, x.cu_k, causal)
+    u = U["bf16"]
+    assert_grad_parity(dq, rq, eq, u, f"varlen {case} dq")
+    assert_grad_parity(dk, rk, ek, u, f"varlen {case} dk")
+    assert_grad_parity(dv, rv, ev, u, f"varlen {case} dv")
+
+
+def test_bwd_varlen_equal_lengths_bitwise_equal_dense(aa):
+    B, S, Hq, Hkv, d = 3, 333, 4, 2, 128
+    x = wl.make_varlen([S] * B, [S] * B, Hq, Hkv, d, seed=811)
+    do = wl.make_grad_out(x.q, 812)
+    got = run_bwd_varlen(aa, x, do, True)
+    xd = wl.make_prefill(B, Hq, Hkv, d, S, S, seed=811)  # same streams and sizes: the same bits
+    assert np.array_equal(xd.q.reshape(x.q.shape), x.q) and np.array_equal(xd.k.reshape(x.k.shape), x.k)
+    ref = run_bwd(aa, xd, do.reshape(B, S, Hq, d), True)
+    for a, r in zip(got, ref):
+        assert np.array_equal(a, r.reshape(a.shape))

@@ -163,3 +163,20 @@ def test_backward_error_scales_bound_the_gradients():
         assert np.all(np.abs(dq) <= eq + 1e-12)
         # and they are not vacuous: within a modest factor of the gradients' own size
         assert ev.max() < 50 * np.abs(dv).max() and ek.max() < 200 * np.abs(dk).max()
+
+
+def test_backward_varlen_equal_lengths_match_batched():
+    """A packed batch of equal-length sequences has the batched [B, S, H, d] gradients."""
+    B, S, Hq, Hkv, d = 3, 21, 4, 2, 8
+    x = wl.make_varlen([S] * B, [S] * B, Hq, Hkv, d, seed=81)
+    do = wl.make_grad_out(x.q, 82)
+    got = oracle.attention_backward_varlen(x.q, x.k, x.v, do, x.cu_q, x.cu_k, True)
+    ref = oracle.attention_backward(x.q.reshape(B, S, Hq, d), x.k.reshape(B, S, Hkv, d), x.v.reshape(B, S, Hkv, d),
+                                    do.reshape(B, S, Hq, d), True)
+    for a, r, n in zip(got, ref[:3], (Hq, Hkv, Hkv)):
+        assert np.array_equal(a, r.reshape(B * S, n, d))
+    es = oracle.backward_error_scales_varlen(x.q, x.k, x.v, do, x.cu_q, x.cu_k, True)
+    er = oracle.backward_error_scales(x.q.reshape(B, S, Hq, d), x.k.reshape(B, S, Hkv, d), x.v.reshape(B, S, Hkv, d),
+                                      do.reshape(B, S, Hq, d), True)
+    for a, r, n in zip(es, er, (Hq, Hkv, Hkv)):
+        assert np.array_equal(a, r.reshape(B * S, n, d))
