@@ -144,11 +144,15 @@ bwd_pre(const uint16_t *__restrict__ o, const uint16_t *__restrict__ dout, const
 // ---------------------------------------------------------------------------
 // dK, dV. Work-group = 4 waves x 32 keys = one 128-key tile of (b, KV head g);
 // query tiles of 32 rows of each of the G query heads of g pass through LDS.
-constexpr int kKT = 128;  // keys per dK/dV work-group
 constexpr int kQB = 32;   // query rows per dK/dV step
+// Keys per dK/dV work-group (32 per wave) and its threads. At d = 128 eight
+// waves share each staged Q/dO tile (one work-group per CU, two waves per
+// SIMD); at d = 64 four (two work-groups per CU).
+template <int D> constexpr int kKT = D == 128 ? 256 : 128;
+template <int D> constexpr int kDkdvThreads = 2 * kKT<D>;
 
 template <int D, bool F16>
-__global__ void __launch_bounds__(256, 2)
+__global__ void __launch_bounds__(kDkdvThreads<D>, kDkdvThreads<D> == 512 ? 1 : 2)
 bwd_dkdv(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
          const uint16_t *__restrict__ dout, const float *__restrict__ l2ws, const float *__restrict__ dws,
          uint16_t *__restrict__ dk, uint16_t *__restrict__ dv, const int *__restrict__ cu_q,
@@ -156,11 +160,12 @@ bwd_dkdv(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const u
          int causal, float scale_log2, float scale, int BHkv) {
   constexpr int KST = D / 16, MT = D / 32, CH = D / 8;
   constexpr int QT = kQB * D;                 // one Q (or dO) tile, elements
-  constexpr int LPT = kQB * CH / 256;         // 16-byte chunks per thread per tile
+  constexpr int NTH = kDkdvThreads<D>, KTL = kKT<D>;
+  constexpr int LPT = kQB * CH / NTH;         // 16-byte chunks per thread per tile
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * QT];  // {Q, dO} x 2 slots
   __shared__ __attribute__((aligned(16))) float stat[2][2][kQB];       // {L2, D} of the step's rows x 2 slots
   constexpr bool kVinLds = D == 128;  // V rows as an LDS tile instead of registers (register budget)
-  __shared__ __attribute__((aligned(16))) uint16_t vres[kVinLds ? kKT * D : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t vres[kVinLds ? KTL * D : 8];
 
   const int x = blockIdx.x;
   const int kt = x / BHkv;  // key tile 0 first: under a causal mask it has the most queries
@@ -176,13 +181,13 @@ bwd_dkdv(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const u
     const int a0 = min(max(cu_q[b], 0), total_q), a1 = min(max(cu_q[b + 1], a0), total_q);
     const int c0 = min(max(cu_k[b], 0), total_k), c1 = min(max(cu_k[b + 1], c0), total_k);
     qbase = a0, Sq = a1 - a0, kbase = c0, Sk = c1 - c0, stat_b = (size_t)a0;
-    if (kt * kKT >= Sk) return;  // the whole work-group: this sequence has fewer key tiles
+    if (kt * KTL >= Sk) return;  // the whole work-group: this sequence has fewer key tiles
   } else {
     qbase = b * Sq, kbase = b * Sk, stat_b = (size_t)b * Hq * Sq_pad;
   }
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, hl = lane >> 5;
-  const int k0 = kt * kKT, kw0 = k0 + 32 * w;  // first key of the tile, of the wave
+  const int k0 = kt * KTL, kw0 = k0 + 32 * w;  // first key of the tile, of the wave
   const int key = kw0 + n;
   const int off = Sk - Sq;
 
@@ -200,7 +205,7 @@ bwd_dkdv(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const u
       // The work-group's 128 V rows, swizzled like the streamed tiles; read
       // row-wise (16 consecutive rows per chunk) as the dP operand.
       const size_t vbase = ((size_t)kbase * Hkv + g) * D;
-      for (int c = tid; c < kKT * CH; c += 256) {
+      for (int c = tid; c < KTL * CH; c += NTH) {
         const int r = c / CH, ch = c % CH, kr = k0 + r;
         const uint4 val = kr < Sk ? ldg16(v + vbase + (size_t)kr * Hkv * D + ch * 8) : make_uint4(0, 0, 0, 0);
         sts16(vres + tile_off<D>(r, ch), val);
@@ -232,7 +237,7 @@ bwd_dkdv(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const u
     const auto rq = buffer_rsrc(q + base, left), rd = buffer_rsrc(dout + base, left);
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
-      const int boff = (int)(((trow + i * (256 / CH)) * rstride + tch * 8) * 2);
+      const int boff = (int)(((trow + i * (NTH / CH)) * rstride + tch * 8) * 2);
       sq[i] = buf_load16(rq, boff);
       sdo[i] = buf_load16(rd, boff);
     }
@@ -241,7 +246,7 @@ bwd_dkdv(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const u
     uint16_t *qt = smem + slot * 2 * QT, *dt = qt + QT;
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
-      const int r = trow + i * (256 / CH);
+      const int r = trow + i * (NTH / CH);
       sts16(qt + tile_off<D>(r, tch), sq[i]);
       sts16(dt + tile_off<D>(r, tch), sdo[i]);
     }
@@ -370,11 +375,15 @@ bwd_dkdv(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const u
 // ---------------------------------------------------------------------------
 // dQ. Work-group = 4 waves x 32 query rows = one 128-row tile of (b, head h);
 // 64-key K and V tiles pass through LDS.
-constexpr int kQT = 128;  // query rows per dQ work-group
-constexpr int kKB = 64;   // keys per dQ step
+// Query rows per dQ work-group (32 per wave) and its threads, as for dK/dV:
+// eight waves at d = 128, four at d = 64.
+template <int D> constexpr int kQT = D == 128 ? 256 : 128;
+template <int D> constexpr int kDqThreads = 2 * kQT<D>;
+constexpr int kKB = 64;    // keys per dQ step
+constexpr int kPad = 128;  // row padding of the statistics workspace
 
 template <int D, bool F16>
-__global__ void __launch_bounds__(256, 2)
+__global__ void __launch_bounds__(kDqThreads<D>, kDqThreads<D> == 512 ? 1 : 2)
 bwd_dq(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
        const uint16_t *__restrict__ dout, const float *__restrict__ l2ws, const float *__restrict__ dws,
        uint16_t *__restrict__ dq, const int *__restrict__ cu_q, const int *__restrict__ cu_k, int total_q,
@@ -382,7 +391,8 @@ bwd_dq(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uin
        int n_qtiles, int BH) {
   constexpr int KST = D / 16, MT = D / 32, CH = D / 8;
   constexpr int KTL = kKB * D;          // one K (or V) tile, elements
-  constexpr int LPT = kKB * CH / 256;   // 16-byte chunks per thread per tile
+  constexpr int NTH = kDqThreads<D>, QTL = kQT<D>;
+  constexpr int LPT = kKB * CH / NTH;   // 16-byte chunks per thread per tile
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * KTL];  // {K, V} x 2 slots
 
   const int x = blockIdx.x;
@@ -392,7 +402,7 @@ bwd_dq(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uin
   const int gk = h / (Hq / Hkv);
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, hl = lane >> 5;
-  const int q0 = qt_ * kQT, r0 = q0 + 32 * w;
+  const int q0 = qt_ * QTL, r0 = q0 + 32 * w;
   const int qrow = r0 + n;
   int qbase, kbase;  // as in bwd_dkdv
   size_t stat_b;
@@ -416,17 +426,18 @@ bwd_dq(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uin
       doop[kk] = ok ? ldg16(dout + roff + (2 * kk + hl) * 8) : make_uint4(0, 0, 0, 0);
     }
   }
-  // In range for every row of the tile (the padding covers a full tile past
-  // the last row); a row past Sq is masked whatever value it reads.
-  const float l2 = l2ws[stat_b + (size_t)h * Sq_pad + qrow];
-  const float Dr = dws[stat_b + (size_t)h * Sq_pad + qrow];
+  // A row past Sq reads the last row's values (it is masked whatever it
+  // reads), so every read stays inside the sequence's statistics.
+  const int qs = min(qrow, Sq - 1);
+  const float l2 = l2ws[stat_b + (size_t)h * Sq_pad + qs];
+  const float Dr = dws[stat_b + (size_t)h * Sq_pad + qs];
   f32x16 dqT[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) dqT[mt][r] = 0.f;
 
-  int kend = causal ? min(Sk, q0 + kQT + off) : Sk;  // keys any row of the tile sees
+  int kend = causal ? min(Sk, q0 + QTL + off) : Sk;  // keys any row of the tile sees
   if (kend < 0) kend = 0;
   const int nblk = (kend + kKB - 1) / kKB;
   // Keys a row of this wave can see: j <= r0 + 31 + off.
@@ -442,7 +453,7 @@ bwd_dq(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uin
     const auto rk = buffer_rsrc(k + base, left), rv = buffer_rsrc(v + base, left);
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
-      const int boff = (int)(((trow + i * (256 / CH)) * rstride + tch * 8) * 2);
+      const int boff = (int)(((trow + i * (NTH / CH)) * rstride + tch * 8) * 2);
       sk[i] = buf_load16(rk, boff);
       sv[i] = buf_load16(rv, boff);
     }
@@ -451,7 +462,7 @@ bwd_dq(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uin
     uint16_t *ktl = smem + slot * 2 * KTL, *vtl = ktl + KTL;
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
-      const int r = trow + i * (256 / CH);
+      const int r = trow + i * (NTH / CH);
       sts16(ktl + tile_off<D>(r, tch), sk[i]);
       sts16(vtl + tile_off<D>(r, tch), sv[i]);
     }
@@ -539,10 +550,10 @@ bwd_dq(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uin
 
 }  // namespace
 
-int bwd_sq_pad(int Sq) { return (Sq + kQT - 1) / kQT * kQT; }
-// Packed batches: one [Hq][pad] statistics block over all rows, padded by a
-// full query tile past the last row (a tile's reads may start at any row).
-int bwd_varlen_pad(int total_q) { return (total_q + kQT + kQT - 1) / kQT * kQT; }
+int bwd_sq_pad(int Sq) { return (Sq + kPad - 1) / kPad * kPad; }
+// Packed batches: one [Hq][pad] statistics block over all rows, padded past
+// the last row (a dK/dV step reads its 32 rows from any starting row).
+int bwd_varlen_pad(int total_q) { return (total_q + kPad + kPad - 1) / kPad * kPad; }
 
 // Dense when cu_q == nullptr: Sq, Sk are the per-sequence lengths. Packed
 // otherwise: Sq, Sk are the longest lengths (they size the grids) and
@@ -572,14 +583,15 @@ hipError_t launch_bwd(const void *q, const void *k, const void *v, const void *o
       hipLaunchKernelGGL(bwd_pre<64>, grid, dim3(256), 0, stream, oo, gg, lse, l2ws, dws, pb, psq, Sq_pad, Hq, f16);
   }
   const int BHkv = batch * Hkv, BH = batch * Hq;
-  const int n_ktiles = (Sk + kKT - 1) / kKT, n_qtiles = (Sq + kQT - 1) / kQT;
+  const int kt_keys = d == 128 ? kKT<128> : kKT<64>, qt_rows = d == 128 ? kQT<128> : kQT<64>;
+  const int n_ktiles = (Sk + kt_keys - 1) / kt_keys, n_qtiles = (Sq + qt_rows - 1) / qt_rows;
   auto dkdv = [&](auto kern) {
-    hipLaunchKernelGGL(kern, dim3(n_ktiles * BHkv), dim3(256), 0, stream, qq, kk, vv, gg, l2ws, dws,
+    hipLaunchKernelGGL(kern, dim3(n_ktiles * BHkv), dim3(2 * kt_keys), 0, stream, qq, kk, vv, gg, l2ws, dws,
                        static_cast<uint16_t *>(dk), static_cast<uint16_t *>(dv), cu_q, cu_k, total_q, total_k, Sq,
                        Sq_pad, Sk, Hq, Hkv, causal, scale_log2, scale, BHkv);
   };
   auto dqk = [&](auto kern) {
-    hipLaunchKernelGGL(kern, dim3(n_qtiles * BH), dim3(256), 0, stream, qq, kk, vv, gg, l2ws, dws,
+    hipLaunchKernelGGL(kern, dim3(n_qtiles * BH), dim3(2 * qt_rows), 0, stream, qq, kk, vv, gg, l2ws, dws,
                        static_cast<uint16_t *>(dq), cu_q, cu_k, total_q, total_k, Sq, Sq_pad, Sk, Hq, Hkv, causal,
                        scale_log2, scale, n_qtiles, BH);
   };
