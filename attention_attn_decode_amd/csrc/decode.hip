@@ -444,7 +444,6 @@ combine_pieces(const float *__restrict__ ws_o, const float2 *__restrict__ ws_ml,
                uint16_t *__restrict__ o, float *__restrict__ lse, int B, int Hq, int Hkv, int sq,
                int max_len, int P, int min_units) {
   constexpr int SEG = D / 16;
-  __shared__ float s_m[kCols], s_l[kCols];
   __shared__ __attribute__((aligned(16))) float s_acc[kCols][D];
   __shared__ float s_gm[kCols], s_gl[kCols];
   const int b = blockIdx.x, g = blockIdx.y;
@@ -452,11 +451,14 @@ combine_pieces(const float *__restrict__ ws_o, const float2 *__restrict__ ws_ml,
   const int G = Hq / Hkv, ncol = G * sq;
   const int NG = kCols / ncol;  // piece groups (>= 1)
   const int col = rest % ncol, grp = rest / ncol;
+  // The plan values are read together with the length (one memory round
+  // trip, not two); for an empty sequence meta[1 + b] was never written and
+  // is not used.
   const int L = clamp_len(seqlens[b], max_len);
+  const long long T = P > 1 ? meta[0] : 0, st = P > 1 ? meta[1 + b] : 0;
   int w0 = 0, w1 = -1;
   if (L > 0) {
     if (P <= 1) return;  // every sequence was finished by the split kernel
-    const long long T = meta[0], st = meta[1 + b];
     const int P_eff = pieces_for(T, P, min_units);
     w0 = piece_of(st, T, P_eff);
     w1 = piece_of(st + units_of(L) - 1, T, P_eff);
@@ -528,8 +530,6 @@ combine_pieces(const float *__restrict__ ws_o, const float2 *__restrict__ ws_ml,
     *reinterpret_cast<uint32_t *>(dst + e) = pack2<F16>(acc[e] * inv, acc[e + 1] * inv);
   if (lse != nullptr && (tid & 15) == 0)
     lse[((size_t)b * Hq + chead) * sq + ct] = lsum > 0.f ? kLn2 * (M + __log2f(lsum)) : kNegInf;
-  (void)s_m;
-  (void)s_l;
 }
 
 }  // namespace
