@@ -47,8 +47,14 @@ int check_decode_shape(int n_q_heads, int n_kv_heads, int d, int seqlen_q, int b
   if (n_q_heads % n_kv_heads != 0) return ATTN_ERR_INVALID;
   if (batch > ATTN_MAX_BATCH || n_kv_heads > 65535) return ATTN_ERR_UNSUPPORTED;
   if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
-  if ((long)(n_q_heads / n_kv_heads) * seqlen_q > 16) return ATTN_ERR_UNSUPPORTED;
+  if ((long)(n_q_heads / n_kv_heads) * seqlen_q > 32) return ATTN_ERR_UNSUPPORTED;
   return ATTN_OK;
+}
+
+// Packed query columns per partial slot: one group of 16, or two when the
+// packed rows (G * seqlen_q) exceed 16.
+unsigned decode_cols(int n_q_heads, int n_kv_heads, int seqlen_q) {
+  return (n_q_heads / n_kv_heads) * seqlen_q > 16 ? 32u : 16u;
 }
 
 int plan_pieces(int n_kv_heads, int d, int num_splits) {
@@ -60,9 +66,9 @@ int plan_pieces(int n_kv_heads, int d, int num_splits) {
 
 // Partial outputs, then (max, denominator) pairs, then the key total and the
 // flattened start of every sequence (int64).
-size_t workspace_bytes_for(int batch, int n_kv_heads, int d, int pieces) {
+size_t workspace_bytes_for(int batch, int n_kv_heads, int d, int pieces, unsigned cols) {
   if (pieces <= 1) return 0;
-  return (size_t)n_kv_heads * (size_t)(pieces + batch) * 16u * (size_t)(d + 2) * 4u +
+  return (size_t)n_kv_heads * (size_t)(pieces + batch) * cols * (size_t)(d + 2) * 4u +
          (size_t)(batch + 1) * 8u;
 }
 
@@ -85,7 +91,8 @@ size_t attn_decode_workspace_size(int batch, int n_q_heads, int n_kv_heads, int 
   if (num_splits < 0 ||
       check_decode_shape(n_q_heads, n_kv_heads, d, seqlen_q, batch, max_seqlen_k) != ATTN_OK)
     return 0;
-  return workspace_bytes_for(batch, n_kv_heads, d, plan_pieces(n_kv_heads, d, num_splits));
+  return workspace_bytes_for(batch, n_kv_heads, d, plan_pieces(n_kv_heads, d, num_splits),
+                             decode_cols(n_q_heads, n_kv_heads, seqlen_q));
 }
 
 }  // extern "C"
@@ -105,13 +112,14 @@ int decode_impl(const void *q, const void *k_cache, const void *v_cache, const i
   // Without a workspace, one piece per KV head: every sequence is finished by
   // the wave that streams it and no partial is stored.
   const int pieces = workspace ? plan_pieces(n_kv_heads, d, num_splits) : 1;
-  const size_t need = workspace_bytes_for(batch, n_kv_heads, d, pieces);
+  const unsigned cols = decode_cols(n_q_heads, n_kv_heads, seqlen_q);
+  const size_t need = workspace_bytes_for(batch, n_kv_heads, d, pieces, cols);
   if (workspace_bytes < need) return ATTN_ERR_WORKSPACE;
   float *ws_o = nullptr;
   float2 *ws_ml = nullptr;
   long long *meta = nullptr;
   if (need > 0) {
-    const size_t slots = (size_t)n_kv_heads * (pieces + batch) * 16u;
+    const size_t slots = (size_t)n_kv_heads * (pieces + batch) * cols;
     ws_o = static_cast<float *>(workspace);
     ws_ml = reinterpret_cast<float2 *>(ws_o + slots * d);
     meta = reinterpret_cast<long long *>(ws_ml + slots);
@@ -325,7 +333,7 @@ const char *attn_status_string(int status) {
   switch (status) {
     case ATTN_OK: return "ok";
     case ATTN_ERR_INVALID: return "invalid argument";
-    case ATTN_ERR_UNSUPPORTED: return "unsupported shape (d must be 64 or 128; packed query rows <= 16)";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported shape (d must be 64 or 128; packed query rows <= 32)";
     case ATTN_ERR_MISALIGNED: return "pointer not 16-byte aligned";
     case ATTN_ERR_WORKSPACE: return "workspace too small";
     case ATTN_ERR_LAUNCH: return "HIP kernel launch failed";

@@ -8,7 +8,8 @@
 // Operand swap ([GQA-SM100] §Starting with the simple pipeline and the
 // introduction): S^T = K Q^T / sqrt(d) and O^T = V^T P^T, so key positions run
 // along the MFMA's M dimension and the small packed query group (the G = Hq/Hkv
-// heads of one KV head times the seqlen_q new tokens, at most 16) along N. With
+// heads of one KV head times the seqlen_q new tokens, at most 32) along N, in
+// one or two groups of 16 columns that share every K and V operand read. With
 // v_mfma_f32_16x16x32_bf16 a lane then owns one query column: the column max and
 // sum over keys are mostly in-lane, the rescale factor of O^T is one scalar per
 // lane, and P leaves the S^T accumulator already in the layout the P*V MFMA
@@ -47,7 +48,7 @@ namespace {
 
 constexpr int kWaves = 4;  // waves (independent workers) per work-group
 constexpr int kSub = 32;   // keys per sub-block
-constexpr int kCols = 16;  // packed query columns
+constexpr int kCols = 16;  // packed query columns per column group
 constexpr int kMaxBatch = 8192;  // sequences per call (lengths staged in LDS)
 
 // XOR swizzle of the 16-byte chunk index of K row r in the LDS tile [32][D]:
@@ -172,7 +173,7 @@ __device__ bool next_segment(Seg &s, const int *lens, int B, long long r1) {
   return false;
 }
 
-template <int D>
+template <int D, int NC>
 struct Slot {
   static constexpr int CH = D / 8;
   static constexpr int RPI = 64 / CH;    // rows one wave-wide 16-byte load covers
@@ -181,17 +182,20 @@ struct Slot {
   static constexpr int KST = D / 32;     // QK k-steps
   uint4 k[NK];
   uint4 v[NVG][4];
-  uint4 q[KST];
+  uint4 q[NC][KST];
 };
 
-template <int D, bool F16>
+// NC column groups of 16 packed query columns (1 or 2); the partial
+// workspace holds 16 * NC columns per slot.
+template <int D, bool F16, int NC>
 __global__ void __launch_bounds__(256, 1)
 decode_stream(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
               const uint16_t *__restrict__ vc, const int *__restrict__ seqlens,
               uint16_t *__restrict__ o, float *__restrict__ lse, float *__restrict__ ws_o,
               float2 *__restrict__ ws_ml, long long *__restrict__ meta, int B, int Hq, int Hkv,
               int sq, int max_len, int P, int min_units, float scale_log2) {
-  using S = Slot<D>;
+  using S = Slot<D, NC>;
+  constexpr int COLS = kCols * NC;
   constexpr int CH = S::CH, RPI = S::RPI, NK = S::NK, NVG = S::NVG, KST = S::KST;
   constexpr int MT = D / 16;
   constexpr int TILE = kSub * D;
@@ -216,9 +220,17 @@ decode_stream(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
 
   const int G = Hq / Hkv, ncol = G * sq;
   const int n = lane & 15, gq = lane >> 4;
-  const bool col_ok = n < ncol;
-  const int tn = col_ok ? n / G : 0;
-  const int head = g * G + (col_ok ? n % G : 0);
+  // Packed column nc[c] = 16 c + n of column group c: new token tn[c], query
+  // head head[c] (pad columns read column 0 and are never written out).
+  bool col_ok[NC];
+  int nc[NC], tn[NC], head[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    nc[c] = kCols * c + n;
+    col_ok[c] = nc[c] < ncol;
+    tn[c] = col_ok[c] ? nc[c] / G : 0;
+    head[c] = g * G + (col_ok[c] ? nc[c] % G : 0);
+  }
   const size_t rstride = (size_t)Hkv * D;
   const int slots = P + B;  // partial slots per KV head
   uint16_t *klds = smem + wv * 2 * TILE;
@@ -246,17 +258,23 @@ decode_stream(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
       }
     }
     // Q^T B operand of this sequence: slot k of lane group gq at k-step kk
-    // covers chunk 4 * kk + gq of the query row (pad columns read column 0
-    // and are never written out).
-    const uint16_t *qrow = q + ((size_t)(b * sq + tn) * Hq + head) * D;
+    // covers chunk 4 * kk + gq of the query row.
 #pragma unroll
-    for (int kk = 0; kk < KST; ++kk) sl.q[kk] = ldg16(qrow + (4 * kk + gq) * 8);
+    for (int c = 0; c < NC; ++c) {
+      const uint16_t *qrow = q + ((size_t)(b * sq + tn[c]) * Hq + head[c]) * D;
+#pragma unroll
+      for (int kk = 0; kk < KST; ++kk) sl.q[c][kk] = ldg16(qrow + (4 * kk + gq) * 8);
+    }
   };
 
-  float m_run = kNegInf, l_run = 0.f;
-  f32x4 oacc[MT];
+  float m_run[NC], l_run[NC];
+  f32x4 oacc[NC][MT];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) oacc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < NC; ++c) {
+    m_run[c] = kNegInf, l_run[c] = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) oacc[c][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   auto compute_slot = [&](const S &sl, const Seg &cs, int j0, bool live) {
     // K registers -> LDS (row-major, swizzled chunks).
@@ -277,54 +295,61 @@ decode_stream(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
     }
     wave_lds_sync();
 
-    f32x4 sacc[2];
+    f32x4 sacc[NC][2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < NC; ++c) sacc[c][t] = f32x4{0.f, 0.f, 0.f, 0.f};
       const int i = lane & 15;
       const int r = 8 * (i >> 2) + 4 * t + (i & 3);
 #pragma unroll
       for (int kk = 0; kk < KST; ++kk) {
-        const int c = 4 * kk + gq;
-        sacc[t] = mma16<F16>(lds16(klds + r * D + ((c ^ k_swz<D>(r)) * 8)), sl.q[kk], sacc[t]);
+        const int ck = 4 * kk + gq;
+        const uint4 ka = lds16(klds + r * D + ((ck ^ k_swz<D>(r)) * 8));
+#pragma unroll
+        for (int c = 0; c < NC; ++c) sacc[c][t] = mma16<F16>(ka, sl.q[c][kk], sacc[c][t]);
       }
     }
 
-    // Keys visible to this column: below the segment end and, among the sq
-    // new tokens, the bottom-right causal limit j <= L - sq + t
-    // ([FA4-edges] §Edge 1: masked to -inf before the max).
-    const int bound = live ? min(cs.hi, cs.L - sq + tn + 1) : 0;
-    float sv[8];
-    float mloc = kNegInf;
+    uint4 pop[NC];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int c = 0; c < NC; ++c) {
+      // Keys visible to this column: below the segment end and, among the sq
+      // new tokens, the bottom-right causal limit j <= L - sq + t
+      // ([FA4-edges] §Edge 1: masked to -inf before the max).
+      const int bound = live ? min(cs.hi, cs.L - sq + tn[c] + 1) : 0;
+      float sv[8];
+      float mloc = kNegInf;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int pos = j0 + 8 * gq + 4 * t + r;
-        const float xs = pos < bound ? sacc[t][r] * scale_log2 : kNegInf;
-        sv[4 * t + r] = xs;
-        mloc = fmaxf(mloc, xs);
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int pos = j0 + 8 * gq + 4 * t + r;
+          const float xs = pos < bound ? sacc[c][t][r] * scale_log2 : kNegInf;
+          sv[4 * t + r] = xs;
+          mloc = fmaxf(mloc, xs);
+        }
+      mloc = wave_xor_max(mloc, 16);
+      mloc = wave_xor_max(mloc, 32);
+      // Online softmax in base 2 ([FA4-edges] §The correction).
+      const float m_new = fmaxf(m_run[c], mloc);
+      const float m_use = m_new == kNegInf ? 0.f : m_new;
+      const float alpha = exp2_hw(m_run[c] - m_use);
+      float p[8], psum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        p[i] = exp2_hw(sv[i] - m_use);
+        psum += p[i];
       }
-    mloc = wave_xor_max(mloc, 16);
-    mloc = wave_xor_max(mloc, 32);
-    // Online softmax in base 2 ([FA4-edges] §The correction).
-    const float m_new = fmaxf(m_run, mloc);
-    const float m_use = m_new == kNegInf ? 0.f : m_new;
-    const float alpha = exp2_hw(m_run - m_use);
-    float p[8], psum = 0.f;
+      l_run[c] = l_run[c] * alpha + psum;
+      m_run[c] = m_new;
+      // Rescale O before accumulating into it ([FA4-edges] §The value MMA waits
+      // on three gates).
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      p[i] = exp2_hw(sv[i] - m_use);
-      psum += p[i];
+      for (int mt = 0; mt < MT; ++mt) oacc[c][mt] *= alpha;
+      pop[c] = make_uint4(pack2<F16>(p[0], p[1]), pack2<F16>(p[2], p[3]), pack2<F16>(p[4], p[5]),
+                          pack2<F16>(p[6], p[7]));
     }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    // Rescale O before accumulating into it ([FA4-edges] §The value MMA waits
-    // on three gates).
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) oacc[mt] *= alpha;
-    const uint4 pop = make_uint4(pack2<F16>(p[0], p[1]), pack2<F16>(p[2], p[3]),
-                                 pack2<F16>(p[4], p[5]), pack2<F16>(p[6], p[7]));
     // A operand: the same eight keys 8gq .. 8gq + 7 at column 16mt + (lane % 16),
     // as two transposed 4-key reads.
     const int trk = lane & 15;
@@ -337,7 +362,9 @@ decode_stream(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
         const int c = 2 * mt + ((trk & 3) >> 1);
         tr[uu] = lds_tr4(vlds + r * D + ((c ^ v_swz<D>(r)) * 8) + 4 * (trk & 1));
       }
-      oacc[mt] = mma16<F16>(make_uint4(tr[0].x, tr[0].y, tr[1].x, tr[1].y), pop, oacc[mt]);
+      const uint4 va = make_uint4(tr[0].x, tr[0].y, tr[1].x, tr[1].y);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) oacc[c][mt] = mma16<F16>(va, pop[c], oacc[c][mt]);
     }
     wave_lds_sync();
   };
@@ -346,33 +373,37 @@ decode_stream(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
   // piece touches it: write the final O and LSE. Otherwise write this wave's
   // partial for sequence b to slot wp + b of KV head g. Then reset the state.
   auto finalize = [&](const Seg &sg) {
-    float l_col = wave_xor_sum(l_run, 16);
-    l_col = wave_xor_sum(l_col, 32);
     const int b = sg.b;
     if (meta != nullptr && sg.lo == 0 && g == 0 && lane == 0) meta[1 + b] = sg.start;
-    if (sg.lo == 0 && sg.hi == sg.L) {
-      if (col_ok) {
-        const float inv = l_col > 0.f ? 1.f / l_col : 0.f;
-        uint16_t *dst = o + ((size_t)(b * sq + tn) * Hq + head) * D;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          *reinterpret_cast<uint2 *>(dst + 16 * mt + 4 * gq) =
-              make_uint2(pack2<F16>(oacc[mt][0] * inv, oacc[mt][1] * inv),
-                         pack2<F16>(oacc[mt][2] * inv, oacc[mt][3] * inv));
-        if (lse != nullptr && gq == 0)
-          lse[((size_t)b * Hq + head) * sq + tn] = l_col > 0.f ? kLn2 * (m_run + __log2f(l_col)) : kNegInf;
+    for (int c = 0; c < NC; ++c) {
+      float l_col = wave_xor_sum(l_run[c], 16);
+      l_col = wave_xor_sum(l_col, 32);
+      if (sg.lo == 0 && sg.hi == sg.L) {
+        if (col_ok[c]) {
+          const float inv = l_col > 0.f ? 1.f / l_col : 0.f;
+          uint16_t *dst = o + ((size_t)(b * sq + tn[c]) * Hq + head[c]) * D;
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+            *reinterpret_cast<uint2 *>(dst + 16 * mt + 4 * gq) =
+                make_uint2(pack2<F16>(oacc[c][mt][0] * inv, oacc[c][mt][1] * inv),
+                           pack2<F16>(oacc[c][mt][2] * inv, oacc[c][mt][3] * inv));
+          if (lse != nullptr && gq == 0)
+            lse[((size_t)b * Hq + head[c]) * sq + tn[c]] =
+                l_col > 0.f ? kLn2 * (m_run[c] + __log2f(l_col)) : kNegInf;
+        }
+      } else if (col_ok[c]) {
+        const size_t slot = (size_t)g * slots + wp + b;
+        float *dst = ws_o + (slot * COLS + nc[c]) * D;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) *reinterpret_cast<f32x4 *>(dst + 16 * mt + 4 * gq) = oacc[c][mt];
+        if (gq == 0) ws_ml[slot * COLS + nc[c]] = make_float2(m_run[c], l_col);
       }
-    } else if (col_ok) {
-      const size_t slot = (size_t)g * slots + wp + b;
-      float *dst = ws_o + (slot * kCols + n) * D;
+      m_run[c] = kNegInf;
+      l_run[c] = 0.f;
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) *reinterpret_cast<f32x4 *>(dst + 16 * mt + 4 * gq) = oacc[mt];
-      if (gq == 0) ws_ml[slot * kCols + n] = make_float2(m_run, l_col);
+      for (int mt = 0; mt < MT; ++mt) oacc[c][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    m_run = kNegInf;
-    l_run = 0.f;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) oacc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
   };
 
   const Seg first = find_segment(lens, B, r0, r1);
@@ -437,19 +468,20 @@ decode_stream(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
 // idle threads form extra groups that merge disjoint, fixed subsets of the
 // pieces (w = w0 + grp, w0 + grp + NG, ...), folded together at the end in
 // group order: the result does not depend on timing.
-template <int D, bool F16>
-__global__ void __launch_bounds__(256)
+template <int D, bool F16, int NC>
+__global__ void __launch_bounds__(256 * NC)
 combine_pieces(const float *__restrict__ ws_o, const float2 *__restrict__ ws_ml,
                const long long *__restrict__ meta, const int *__restrict__ seqlens,
                uint16_t *__restrict__ o, float *__restrict__ lse, int B, int Hq, int Hkv, int sq,
                int max_len, int P, int min_units) {
   constexpr int SEG = D / 16;
-  __shared__ __attribute__((aligned(16))) float s_acc[kCols][D];
-  __shared__ float s_gm[kCols], s_gl[kCols];
+  constexpr int COLS = kCols * NC;  // columns per partial slot
+  __shared__ __attribute__((aligned(16))) float s_acc[COLS][D];
+  __shared__ float s_gm[COLS], s_gl[COLS];
   const int b = blockIdx.x, g = blockIdx.y;
   const int tid = threadIdx.x, seg = (tid & 15) * SEG, rest = tid >> 4;
   const int G = Hq / Hkv, ncol = G * sq;
-  const int NG = kCols / ncol;  // piece groups (>= 1)
+  const int NG = COLS / ncol;  // piece groups (>= 1)
   const int col = rest % ncol, grp = rest / ncol;
   // The plan values are read together with the length (one memory round
   // trip, not two); for an empty sequence meta[1 + b] was never written and
@@ -472,8 +504,8 @@ combine_pieces(const float *__restrict__ ws_o, const float2 *__restrict__ ws_ml,
   if (grp < NG) {
 #pragma unroll 4
     for (int w = w0 + grp; w <= w1; w += NG) {
-      const float2 ml = ws_ml[(base + w) * kCols + col];
-      const float *src = ws_o + ((base + w) * kCols + col) * D + seg;
+      const float2 ml = ws_ml[(base + w) * COLS + col];
+      const float *src = ws_o + ((base + w) * COLS + col) * D + seg;
       float x[SEG];
 #pragma unroll
       for (int e = 0; e < SEG; e += 4) {
@@ -549,32 +581,34 @@ hipError_t launch_decode(const void *q, const void *k, const void *v, const int3
   const auto *kk = static_cast<const uint16_t *>(k);
   const auto *vv = static_cast<const uint16_t *>(v);
   auto *oo = static_cast<uint16_t *>(o);
+  // One column group for up to 16 packed query rows, two for up to 32.
+  const bool wide = (Hq / Hkv) * sq > kCols;
   auto split = [&](auto kern) {
     hipLaunchKernelGGL(kern, grid, block, 0, stream, qq, kk, vv, seqlens, oo, lse, ws_o, ws_ml, meta, batch, Hq,
                        Hkv, sq, max_len, pieces, min_units, scale_log2);
   };
   if (d == 128) {
-    if (f16) split(decode_stream<128, true>);
-    else split(decode_stream<128, false>);
+    if (f16) wide ? split(decode_stream<128, true, 2>) : split(decode_stream<128, true, 1>);
+    else wide ? split(decode_stream<128, false, 2>) : split(decode_stream<128, false, 1>);
   } else {
-    if (f16) split(decode_stream<64, true>);
-    else split(decode_stream<64, false>);
+    if (f16) wide ? split(decode_stream<64, true, 2>) : split(decode_stream<64, true, 1>);
+    else wide ? split(decode_stream<64, false, 2>) : split(decode_stream<64, false, 1>);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   // Launched even with one piece per KV head: it writes O = 0 and LSE = -inf
   // for empty sequences, which no split-kernel wave visits.
-  const dim3 cgrid(batch, Hkv);
+  const dim3 cgrid(batch, Hkv), cblock(wide ? 512 : 256);
   auto combine = [&](auto kern) {
-    hipLaunchKernelGGL(kern, cgrid, block, 0, stream, ws_o, ws_ml, meta, seqlens, oo, lse, batch, Hq, Hkv, sq,
+    hipLaunchKernelGGL(kern, cgrid, cblock, 0, stream, ws_o, ws_ml, meta, seqlens, oo, lse, batch, Hq, Hkv, sq,
                        max_len, pieces, min_units);
   };
   if (d == 128) {
-    if (f16) combine(combine_pieces<128, true>);
-    else combine(combine_pieces<128, false>);
+    if (f16) wide ? combine(combine_pieces<128, true, 2>) : combine(combine_pieces<128, true, 1>);
+    else wide ? combine(combine_pieces<128, false, 2>) : combine(combine_pieces<128, false, 1>);
   } else {
-    if (f16) combine(combine_pieces<64, true>);
-    else combine(combine_pieces<64, false>);
+    if (f16) wide ? combine(combine_pieces<64, true, 2>) : combine(combine_pieces<64, true, 1>);
+    else wide ? combine(combine_pieces<64, false, 2>) : combine(combine_pieces<64, false, 1>);
   }
   return hipGetLastError();
 }

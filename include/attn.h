@@ -59,7 +59,7 @@ extern "C" {
 
 #define ATTN_OK 0
 #define ATTN_ERR_INVALID (-1)     /* NULL pointer, a size <= 0, Hq % Hkv != 0, ... */
-#define ATTN_ERR_UNSUPPORTED (-2) /* d not in {64, 128}; packed query rows > 16 */
+#define ATTN_ERR_UNSUPPORTED (-2) /* d not in {64, 128}; packed query rows > 32 */
 #define ATTN_ERR_MISALIGNED (-3)  /* a data pointer not 16-byte aligned */
 #define ATTN_ERR_WORKSPACE (-4)   /* workspace smaller than the plan needs */
 #define ATTN_ERR_LAUNCH (-5)      /* the HIP runtime refused a launch */
@@ -99,9 +99,11 @@ int attn_decode_plan(int batch, int n_q_heads, int n_kv_heads, int d, int seqlen
 /*
  * Bytes of workspace attn_decode_ex(..., num_splits) needs for this shape
  * (attn_decode uses num_splits = 0):
- *   n_kv_heads * (pieces + batch) * 16 * (d + 2) * 4 + (batch + 1) * 8,
- * or 0 when pieces == 1. It holds per-(piece, sequence) fp32 partial outputs,
- * maxima and denominators for the (at most) pieces + batch partials of each KV
+ *   n_kv_heads * (pieces + batch) * C * (d + 2) * 4 + (batch + 1) * 8,
+ * or 0 when pieces == 1, with C = 16 packed columns per partial when
+ * (n_q_heads / n_kv_heads) * seqlen_q <= 16 and C = 32 otherwise. It holds
+ * per-(piece, sequence) fp32 partial outputs, maxima and denominators for
+ * the (at most) pieces + batch partials of each KV
  * head, then the key total and each sequence's flattened start. It needs no
  * initialisation (e.g. torch.empty): every value the combine step reads is
  * written by the same call ([GQA-SM100] §Removing the max reset).
@@ -123,8 +125,10 @@ size_t attn_decode_workspace_size(int batch, int n_q_heads, int n_kv_heads, int 
  *   lse        [batch][n_q_heads][seqlen_q] fp32 natural-log LSE, overwritten;
  *              may be NULL.
  *   The seqlen_q new tokens are causal among themselves (bottom-right mask).
- *   Requires d in {64, 128}, (n_q_heads / n_kv_heads) * seqlen_q <= 16 and
- *   batch <= ATTN_MAX_BATCH (else ATTN_ERR_UNSUPPORTED).
+ *   Requires d in {64, 128}, (n_q_heads / n_kv_heads) * seqlen_q <= 32 (the
+ *   packed query rows of one KV head: one MFMA column group of 16, or two that
+ *   share every K and V read) and batch <= ATTN_MAX_BATCH (else
+ *   ATTN_ERR_UNSUPPORTED).
  *   workspace / workspace_bytes: caller scratch of at least
  *   attn_decode_workspace_size(...) bytes; workspace == NULL means one piece
  *   per KV head (each sequence is streamed whole by one wave; slow on few

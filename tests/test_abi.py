@@ -75,14 +75,20 @@ def test_workspace_size_formula():
     assert aa.attn_decode_workspace_size(0, 8, 1, 1, 64, 100) == 0
     assert aa.attn_decode_workspace_size(1, 8, 1, 1, 64, 0) == 0
     assert aa.attn_decode_workspace_size(1, 8, 3, 1, 64, 10) == 0  # Hq % Hkv != 0
+    # more than 16 packed rows: 32 columns per partial
+    assert aa.attn_decode_workspace_size(4, 32, 1, 1, 128, 131072) == 1 * (896 + 4) * 32 * 130 * 4 + 5 * 8
+    assert aa.attn_decode_workspace_size(2, 16, 2, 4, 64, 4096) == 2 * (512 + 2) * 32 * 66 * 4 + 3 * 8
 
 
 @pytest.mark.parametrize("args,status", [
     ((32, 8, 128, 1, 1, 64), aa.ATTN_OK),
     ((30, 8, 128, 1, 1, 64), aa.ATTN_ERR_INVALID),       # Hq % Hkv
     ((32, 8, 96, 1, 1, 64), aa.ATTN_ERR_UNSUPPORTED),    # d
-    ((32, 8, 128, 5, 1, 64), aa.ATTN_ERR_UNSUPPORTED),   # G * sq = 20 > 16
-    ((16, 1, 64, 1, 1, 64), aa.ATTN_OK),                 # G = 16, the widest group
+    ((32, 8, 128, 5, 1, 64), aa.ATTN_OK),                # G * sq = 20: two column groups
+    ((32, 8, 128, 9, 1, 64), aa.ATTN_ERR_UNSUPPORTED),   # G * sq = 36 > 32
+    ((16, 1, 64, 1, 1, 64), aa.ATTN_OK),                 # G = 16, one column group
+    ((32, 1, 128, 1, 1, 64), aa.ATTN_OK),                # G = 32, the widest group
+    ((64, 1, 128, 1, 1, 64), aa.ATTN_ERR_UNSUPPORTED),   # G = 64
     ((32, 8, 128, 0, 1, 64), aa.ATTN_ERR_INVALID),       # sq = 0
     ((32, 8, 128, 1, 0, 64), aa.ATTN_ERR_INVALID),       # batch = 0
     ((32, 8, 128, 1, 8192, 64), aa.ATTN_OK),             # largest batch

@@ -212,3 +212,49 @@ def test_bwd_varlen_equal_lengths_bitwise_equal_dense(aa):
     ref = run_bwd(aa, xd, do.reshape(B, S, Hq, d), True)
     for a, r in zip(got, ref):
         assert np.array_equal(a, r.reshape(a.shape))
+
+
+def test_hip_graph_replay_forward_and_backward(aa):
+    """attn_fwd + attn_bwd (and their packed forms) captured once, replayed with new dO and a
+    reused workspace, eager work and synchronisation between replays; every replay equals
+    the eager calls bit for bit."""
+    torch = G.torch()
+    B, S, Hq, Hkv, d = 2, 300, 4, 2, 128
+    x = wl.make_prefill(B, Hq, Hkv, d, S, S, seed=901)
+    q, k, v = G.dev_bf16(x.q), G.dev_bf16(x.k), G.dev_bf16(x.v)
+    do = G.dev_bf16(wl.make_grad_out(x.q, 902))
+    o, lse = G.nan_like_bf16(q.shape), G.nan_f32((B, Hq, S))
+    dq, dk, dv = G.nan_like_bf16(q.shape), G.nan_like_bf16(k.shape), G.nan_like_bf16(k.shape)
+    ws = torch.full((aa.attn_bwd_workspace_size(B, Hq, S) // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    xv = wl.make_varlen([S, 77], [S, 90], Hq, Hkv, d, seed=903)
+    qv, kv_, vv = G.dev_bf16(xv.q), G.dev_bf16(xv.k), G.dev_bf16(xv.v)
+    cq, ck = G.dev_i32(xv.cu_q), G.dev_i32(xv.cu_k)
+    ov, lv = G.nan_like_bf16(qv.shape), G.nan_f32((Hq, qv.shape[0]))
+
+    def calls(stream):
+        aa.attn_fwd(q, k, v, o, lse, causal=True, stream=stream)
+        aa.attn_bwd(q, k, v, o, lse, do, dq, dk, dv, ws, causal=True, stream=stream)
+        aa.attn_fwd_varlen(qv, kv_, vv, cq, ck, ov, S, lse=lv, causal=True, stream=stream)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        calls(s)  # warm-up outside capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        calls(s)
+    for rep in range(3):
+        do.copy_(G.dev_bf16(wl.make_grad_out(x.q, 910 + rep)))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [G.host_f64(t) for t in (o, lse, dq, dk, dv, ov, lv)]
+        for t in (o, dq, dk, dv, ov):
+            t.fill_(float("nan"))
+        calls(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        want = [G.host_f64(t) for t in (o, lse, dq, dk, dv, ov, lv)]
+        for i, (a_, b_) in enumerate(zip(got, want)):
+            assert np.array_equal(a_, b_), f"replay {rep}, output {i}"

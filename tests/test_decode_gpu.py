@@ -130,7 +130,7 @@ def test_seqlens_are_clamped_to_capacity(aa):
 @pytest.mark.parametrize("shape", [(16, 1, 1), (8, 2, 4), (4, 4, 4), (1, 1, 1), (2, 1, 8), (32, 2, 1)])
 @pytest.mark.parametrize("d", [64, 128])
 def test_group_shapes(aa, shape, d):
-    """Packed query columns from 1 up to the 16-column maximum, G*sq = 16 included."""
+    """Packed query columns from 1 up to one full 16-column group, G*sq = 16 included."""
     Hq, Hkv, sq = shape
     x = wl.make_decode(2, Hq, Hkv, d, sq, 600, [600, 333], seed=67 + Hq + sq + d)
     check(aa, x, f"Hq={Hq} Hkv={Hkv} sq={sq} d={d}")
@@ -234,3 +234,39 @@ def test_f16_decode_parity(aa, shape, num_splits):
     B, Hq, Hkv, d, sq, S, lens = shape
     x = wl.make_decode(B, Hq, Hkv, d, sq, S, lens, seed=301 + d + sq, dtype="f16")
     check(aa, x, f"f16 {shape} pieces={num_splits}", num_splits=num_splits)
+
+
+# --- more than 16 packed query rows: two column groups sharing the K/V reads ---
+
+WIDE = [
+    # Hq, Hkv, sq, d, lengths
+    (32, 1, 1, 128, [4096, 3000, 17, 2049]),      # MQA-style group of 32
+    (64, 2, 1, 64, [1500, 1, 777]),               # G = 32 at d = 64
+    (8, 1, 4, 64, [4096, 513, 4, 3]),             # 8 heads x 4 new tokens (causal among them)
+    (16, 2, 2, 128, [2048, 1000]),                # G = 8, sq = 2: 16 rows, the one-group boundary
+    (20, 4, 4, 128, [1200, 64, 0, 333]),          # G = 5, sq = 4: 20 rows, a partly used second group
+    (16, 1, 2, 128, [700, 64, 65]),               # G = 16, sq = 2: exactly 32 rows
+]
+
+
+@pytest.mark.parametrize("shape", WIDE)
+def test_wide_groups_against_oracle(aa, shape):
+    Hq, Hkv, sq, d, lens = shape
+    x = wl.make_decode(len(lens), Hq, Hkv, d, sq, max(lens) + 5, lens, seed=601 + Hq + sq, pad=wl.BF16_NAN)
+    check(aa, x, f"wide {shape}")
+
+
+@pytest.mark.parametrize("num_splits", [1, 3, 64])
+def test_wide_group_piece_invariance(aa, num_splits):
+    x = wl.make_decode(3, 32, 1, 128, 1, 5000, [5000, 4096, 1], seed=611, pad=wl.BF16_NAN)
+    ref = run_decode(aa, x, num_splits=0)
+    got = run_decode(aa, x, num_splits=num_splits)
+    O_ref, L_ref = oracle.attention(x.q, x.k, x.v, x.seqlens, True)
+    G.assert_parity(got[0], got[1], O_ref, L_ref, f"wide splits={num_splits}")
+    # piece count changes only the merge order: results agree to rounding
+    assert np.abs(got[0] - ref[0]).max() <= 2e-2
+
+
+def test_wide_group_f16(aa):
+    x = wl.make_decode(2, 32, 1, 128, 1, 3000, [3000, 1234], seed=621, dtype="f16")
+    check(aa, x, "wide f16")
