@@ -23,6 +23,24 @@ def aa():
     return mod
 
 
+def piece_spans(lens, P, max_len, min_piece=64, sub=32):
+    """Pieces each sequence spans under the balanced split (the plan the header
+    documents): sub-blocks of all sequences end to end, cut into P_eff equal
+    pieces. Used only to check that a test reaches the merge paths it names."""
+    n = [-(-min(max(L, 0), max_len) // sub) for L in lens]
+    T = sum(n)
+    if T == 0:
+        return [0] * len(lens)
+    mu = max(1, min_piece // sub)
+    p_eff = max(1, min(P, -(-T // mu)))
+    piece = lambda xx: ((xx + 1) * p_eff - 1) // T
+    out, st = [], 0
+    for nb in n:
+        out.append(piece(st + nb - 1) - piece(st) + 1 if nb else 0)
+        st += nb
+    return out
+
+
 def run_decode(aa, x, num_splits=0, workspace="auto", poison=True):
     torch = G.torch()
     B, sq, Hq, d = x.q.shape
@@ -270,3 +288,26 @@ def test_wide_group_piece_invariance(aa, num_splits):
 def test_wide_group_f16(aa):
     x = wl.make_decode(2, 32, 1, 128, 1, 3000, [3000, 1234], seed=621, dtype="f16")
     check(aa, x, "wide f16")
+
+
+# Sequences spread over many pieces: K partials per sequence, including K = 127
+# and odd counts that leave one piece over in the combine's piece groups.
+MERGE = [
+    # Hq, Hkv, sq, d, lengths, num_splits, the spans K that must occur
+    (16, 2, 2, 128, [576], 9, {9}),
+    (16, 2, 2, 128, [512], 8, {8}),
+    (8, 1, 1, 64, [1024], 16, {16}),
+    (8, 1, 1, 64, [1088], 17, {17}),
+    (32, 1, 1, 128, [8192, 40, 33], 128, {127, 2, 1}),
+    (16, 4, 1, 128, [3000, 64, 4000, 0, 1], 40, {17, 23, 1}),
+]
+
+
+@pytest.mark.parametrize("case", MERGE)
+def test_many_piece_merges_against_oracle(aa, case):
+    Hq, Hkv, sq, d, lens, ns, spans = case
+    S = max(lens) + 3
+    K = piece_spans(lens, ns, S)
+    assert spans <= set(K), (K, spans)
+    x = wl.make_decode(len(lens), Hq, Hkv, d, sq, S, lens, seed=631 + sum(lens) % 97, pad=wl.BF16_NAN)
+    check(aa, x, f"merge K={K}", num_splits=ns)
