@@ -50,6 +50,9 @@ constexpr int kWaves = 4;  // waves (independent workers) per work-group
 constexpr int kSub = 32;   // keys per sub-block
 constexpr int kCols = 16;  // packed query columns per column group
 constexpr int kMaxBatch = 8192;  // sequences per call (lengths staged in LDS)
+// Pieces per sequence (P / B) above which the combine splits each sequence's
+// merge over its output slices instead of one work-group per sequence.
+constexpr int kSliceCombine = 16;
 
 // XOR swizzle of the 16-byte chunk index of K row r in the LDS tile [32][D]:
 // the 16 rows one QK A-operand read touches land on 16 distinct bank groups.
@@ -564,11 +567,110 @@ combine_pieces(const float *__restrict__ ws_o, const float2 *__restrict__ ws_ml,
     lse[((size_t)b * Hq + chead) * sq + ct] = lsum > 0.f ? kLn2 * (M + __log2f(lsum)) : kNegInf;
 }
 
+
+// Combine for calls whose sequences spread over many pieces (few sequences
+// and KV heads, long keys: the batch-1 decode shapes). The merge of one
+// (sequence, KV head) is split over its outputs: one work-group per 16-float
+// slice of one packed column. Its 64 piece lanes (4 threads of one float4
+// each) merge the disjoint, fixed piece subsets w0 + p, w0 + p + 64, ... with
+// the rules of combine_pieces, and the 64 lane states then fold pairwise in a
+// fixed tree through LDS (lane p takes lane p + h for h = 32, 16, ..., 1):
+// the result does not depend on timing.
+template <int D, bool F16, int NC>
+__global__ void __launch_bounds__(256)
+combine_slices(const float *__restrict__ ws_o, const float2 *__restrict__ ws_ml,
+               const long long *__restrict__ meta, const int *__restrict__ seqlens,
+               uint16_t *__restrict__ o, float *__restrict__ lse, int B, int Hq, int Hkv, int sq,
+               int max_len, int P, int min_units) {
+  constexpr int COLS = kCols * NC;  // columns per partial slot
+  constexpr int SPC = D / 16;       // 16-float slices per column
+  constexpr int NP = 64;            // piece lanes
+  constexpr int NB = 4;             // pieces per lane whose loads are in flight together
+  __shared__ __attribute__((aligned(16))) float4 s_acc[NP][4];
+  __shared__ float s_m[NP], s_l[NP];
+  const int b = blockIdx.z, g = blockIdx.y;
+  const int col = blockIdx.x / SPC, sl = blockIdx.x % SPC;
+  const int G = Hq / Hkv, ncol = G * sq;
+  if (col >= ncol) return;
+  const int tid = threadIdx.x, f = tid & 3, p = tid >> 2;
+  const int L = clamp_len(seqlens[b], max_len);
+  const long long T = P > 1 ? meta[0] : 0, st = P > 1 ? meta[1 + b] : 0;
+  int w0 = 0, w1 = -1;
+  if (L > 0) {
+    if (P <= 1) return;
+    const int P_eff = pieces_for(T, P, min_units);
+    w0 = piece_of(st, T, P_eff);
+    w1 = piece_of(st + units_of(L) - 1, T, P_eff);
+    if (w0 == w1) return;
+  }
+  const size_t base = (size_t)g * (P + B) + b;  // slot of piece w is base + w
+  const int eoff = 16 * sl + 4 * f;             // this thread's first output element
+  float M = kNegInf, lsum = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int w = w0 + p; w <= w1; w += NB * NP) {
+    // Pieces past w1 re-read w1's slot and get weight zero.
+    float2 ml[NB];
+    float4 x[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const size_t slot = base + min(w + j * NP, w1);
+      ml[j] = ws_ml[slot * COLS + col];
+      x[j] = *reinterpret_cast<const float4 *>(ws_o + (slot * COLS + col) * D + eoff);
+    }
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const bool live = w + j * NP <= w1 && ml[j].x != kNegInf;
+      const float Mn = live ? fmaxf(M, ml[j].x) : M;
+      const float a = live ? exp2_hw(M - Mn) : 1.f;
+      const float c = live ? exp2_hw(ml[j].x - Mn) : 0.f;
+      lsum = lsum * a + ml[j].y * c;
+      acc.x = acc.x * a + x[j].x * c;
+      acc.y = acc.y * a + x[j].y * c;
+      acc.z = acc.z * a + x[j].z * c;
+      acc.w = acc.w * a + x[j].w * c;
+      M = Mn;
+    }
+  }
+  s_acc[p][f] = acc;
+  if (f == 0) s_m[p] = M, s_l[p] = lsum;
+  for (int h = NP / 2; h >= 1; h >>= 1) {
+    __syncthreads();
+    if (p < h) {
+      const float m2 = s_m[p + h];
+      if (m2 != kNegInf) {
+        const float Mn = fmaxf(M, m2);
+        const float a = exp2_hw(M - Mn), c = exp2_hw(m2 - Mn);
+        const float4 y = s_acc[p + h][f];
+        lsum = lsum * a + s_l[p + h] * c;
+        acc.x = acc.x * a + y.x * c;
+        acc.y = acc.y * a + y.y * c;
+        acc.z = acc.z * a + y.z * c;
+        acc.w = acc.w * a + y.w * c;
+        M = Mn;
+      }
+    }
+    __syncthreads();
+    if (p < h) {
+      s_acc[p][f] = acc;
+      if (f == 0) s_m[p] = M, s_l[p] = lsum;
+    }
+  }
+  if (p != 0) return;
+  const int ct = col / G, chead = g * G + col % G;
+  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+  uint16_t *dst = o + ((size_t)(b * sq + ct) * Hq + chead) * D + eoff;
+  *reinterpret_cast<uint2 *>(dst) = make_uint2(pack2<F16>(acc.x * inv, acc.y * inv), pack2<F16>(acc.z * inv, acc.w * inv));
+  if (lse != nullptr && sl == 0 && f == 0)
+    lse[((size_t)b * Hq + chead) * sq + ct] = lsum > 0.f ? kLn2 * (M + __log2f(lsum)) : kNegInf;
+}
+
 }  // namespace
 
 // Host-side launcher (called by the C ABI after validation). Work-groups:
 // ceil(Hkv * P / 4) for the split kernel (extra waves exit at once when the
-// keys allow fewer pieces), B x Hkv for the combine.
+// keys allow fewer pieces); for the combine, B x Hkv when the pieces per
+// sequence are few (P <= kSliceCombine * B), else one per 16-float output
+// slice of every packed column of every (sequence, KV head).
 hipError_t launch_decode(const void *q, const void *k, const void *v, const int32_t *seqlens,
                          void *o, float *lse, float *ws_o, float2 *ws_ml, long long *meta,
                          int batch, int Hq,
@@ -598,6 +700,22 @@ hipError_t launch_decode(const void *q, const void *k, const void *v, const int3
   if (err != hipSuccess) return err;
   // Launched even with one piece per KV head: it writes O = 0 and LSE = -inf
   // for empty sequences, which no split-kernel wave visits.
+  if (pieces > kSliceCombine * batch) {
+    const int ncol = (Hq / Hkv) * sq;
+    const dim3 sgrid((unsigned)(ncol * (d / 16)), Hkv, batch);
+    auto slices = [&](auto kern) {
+      hipLaunchKernelGGL(kern, sgrid, dim3(256), 0, stream, ws_o, ws_ml, meta, seqlens, oo, lse, batch, Hq, Hkv,
+                         sq, max_len, pieces, min_units);
+    };
+    if (d == 128) {
+      if (f16) wide ? slices(combine_slices<128, true, 2>) : slices(combine_slices<128, true, 1>);
+      else wide ? slices(combine_slices<128, false, 2>) : slices(combine_slices<128, false, 1>);
+    } else {
+      if (f16) wide ? slices(combine_slices<64, true, 2>) : slices(combine_slices<64, true, 1>);
+      else wide ? slices(combine_slices<64, false, 2>) : slices(combine_slices<64, false, 1>);
+    }
+    return hipGetLastError();
+  }
   const dim3 cgrid(batch, Hkv), cblock(wide ? 512 : 256);
   auto combine = [&](auto kern) {
     hipLaunchKernelGGL(kern, cgrid, cblock, 0, stream, ws_o, ws_ml, meta, seqlens, oo, lse, batch, Hq, Hkv, sq,

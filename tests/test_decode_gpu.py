@@ -300,6 +300,10 @@ MERGE = [
     (8, 1, 1, 64, [1088], 17, {17}),
     (32, 1, 1, 128, [8192, 40, 33], 128, {127, 2, 1}),
     (16, 4, 1, 128, [3000, 64, 4000, 0, 1], 40, {17, 23, 1}),
+    # one sequence over every piece of the automatic plan (the batch-1 shapes:
+    # each sequence's merge is split over its output slices)
+    (16, 1, 1, 128, [20000], 0, {313}),
+    (16, 2, 1, 64, [9000, 0], 0, {141, 0}),
 ]
 
 
@@ -307,7 +311,7 @@ MERGE = [
 def test_many_piece_merges_against_oracle(aa, case):
     Hq, Hkv, sq, d, lens, ns, spans = case
     S = max(lens) + 3
-    K = piece_spans(lens, ns, S)
+    K = piece_spans(lens, aa.attn_decode_plan(len(lens), Hq, Hkv, d, sq, S, ns)[0], S)
     assert spans <= set(K), (K, spans)
     x = wl.make_decode(len(lens), Hq, Hkv, d, sq, S, lens, seed=631 + sum(lens) % 97, pad=wl.BF16_NAN)
     check(aa, x, f"merge K={K}", num_splits=ns)
