@@ -129,6 +129,33 @@ __device__ __forceinline__ int chunk_swz(int r) {
   else return (4 * ((r >> 1) & 1)) | ((r >> 2) & 3);
 }
 
+// f(I), f(I + 1), ..., f(N - 1) with the index a compile-time constant.
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+// A stream of NG MFMAs g = 0 .. NG - 1 whose LDS operands are read KDEP MFMAs
+// ahead through a register ring, so no product waits on LDS latency:
+// read(g) returns operand g, mma(g, a) issues product g. With PIN, a schedule
+// barrier after each product keeps the compiler from regrouping the reads
+// next to their uses.
+template <int NG, int KDEP, bool PIN = true, typename R, typename M>
+__device__ __forceinline__ void mfma_stream(R &&read, M &&mma) {
+  uint4 ring[KDEP];
+  static_for<0, (KDEP < NG ? KDEP : NG)>([&](auto gc) { ring[decltype(gc)::value] = read(gc); });
+  static_for<0, NG>([&](auto gc) {
+    constexpr int g = decltype(gc)::value;
+    const uint4 a = ring[g % KDEP];
+    if constexpr (g + KDEP < NG) ring[g % KDEP] = read(std::integral_constant<int, g + KDEP>{});
+    mma(gc, a);
+    if constexpr (PIN) __builtin_amdgcn_sched_barrier(0);
+  });
+}
+
 __device__ __forceinline__ uint4 ldg16(const uint16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
 __device__ __forceinline__ uint4 lds16(const uint16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
 __device__ __forceinline__ void sts16(uint16_t *p, const uint4 &v) { *reinterpret_cast<uint4 *>(p) = v; }

@@ -65,6 +65,11 @@ template <int D> constexpr bool kLateLoads = D == 64;
 // register count past the budget, so every tile takes the masked path.
 template <int D> constexpr bool kUnmaskedPath = D == 64;
 
+// LDS operands read three MFMAs ahead of their product through a register
+// ring (mfma_stream) at d = 64. At d = 128 the ring's registers push both
+// kernels past their budget and the spills cost more than the ring saves.
+template <int D> constexpr bool kOperandRing = D == 64;
+
 __device__ __forceinline__ int pi_row(int i) { return (i & ~12) | ((i >> 1) & 4) | ((i << 1) & 8); }
 
 // Row-major tile of R rows x D elements in LDS, 16-byte chunks XOR-swizzled
@@ -269,15 +274,29 @@ bwd_dkdv(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const u
     const bool active = i0 + kQB - 1 >= wave_first_i && kw0 < Sk;
     if (active) {
       f32x16 S, dP;
+      if constexpr (kOperandRing<D> && !kVinLds) {
+        // S^T = K Q^T and dP^T = V dO^T as one stream (Q and dO rows from LDS).
+        mfma_stream<2 * KST, 3>(
+            [&](auto gc) {
+              constexpr int g = decltype(gc)::value;
+              return tile_row_operand<D>(g % 2 ? dt : qt, lane, 0, g / 2);
+            },
+            [&](auto gc, const uint4 &a) {
+              constexpr int g = decltype(gc)::value, kk = g / 2;
+              if constexpr (g % 2 == 0) S = mma32<F16>(a, kop[kk], kk == 0 ? f32x16{} : S);
+              else dP = mma32<F16>(a, vop[kk], kk == 0 ? f32x16{} : dP);
+            });
+      } else {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) S[r] = 0.f, dP[r] = 0.f;
+        for (int r = 0; r < 16; ++r) S[r] = 0.f, dP[r] = 0.f;
 #pragma unroll
-      for (int kk = 0; kk < KST; ++kk) {
-        S = mma32<F16>(tile_row_operand<D>(qt, lane, 0, kk), kop[kk], S);
-        uint4 vb;
-        if constexpr (kVinLds) vb = lds16(vres + tile_off<D>(32 * w + n, 2 * kk + hl));
-        else vb = vop[kk];
-        dP = mma32<F16>(tile_row_operand<D>(dt, lane, 0, kk), vb, dP);
+        for (int kk = 0; kk < KST; ++kk) {
+          S = mma32<F16>(tile_row_operand<D>(qt, lane, 0, kk), kop[kk], S);
+          uint4 vb;
+          if constexpr (kVinLds) vb = lds16(vres + tile_off<D>(32 * w + n, 2 * kk + hl));
+          else vb = vop[kk];
+          dP = mma32<F16>(tile_row_operand<D>(dt, lane, 0, kk), vb, dP);
+        }
       }
       // Register r holds query i0 + 16 (r / 8) + 8 hl + r % 8.
       const float *l2p = &stat[st & 1][0][8 * hl];
@@ -342,13 +361,27 @@ bwd_dkdv(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const u
       if constexpr (kLateLoads<D>) {
         if (st + 1 < nsteps) load_step(st + 1);
       }
+      if constexpr (kOperandRing<D>) {
+        // dV^T += dO^T P^T and dK^T += Q^T dS^T as one stream.
+        mfma_stream<4 * MT, 3>(
+            [&](auto gc) {
+              constexpr int g = decltype(gc)::value, mt = g / 4, ks = (g / 2) % 2;
+              return tile_tr_operand<D>(g % 2 ? qt : dt, lane, ks, mt);
+            },
+            [&](auto gc, const uint4 &a) {
+              constexpr int g = decltype(gc)::value, mt = g / 4, ks = (g / 2) % 2;
+              if constexpr (g % 2 == 0) dvT[mt] = mma32<F16>(a, pP[ks], dvT[mt]);
+              else dkT[mt] = mma32<F16>(a, pS[ks], dkT[mt]);
+            });
+      } else {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          dvT[mt] = mma32<F16>(tile_tr_operand<D>(dt, lane, ks, mt), pP[ks], dvT[mt]);
-          dkT[mt] = mma32<F16>(tile_tr_operand<D>(qt, lane, ks, mt), pS[ks], dkT[mt]);
-        }
+          for (int ks = 0; ks < 2; ++ks) {
+            dvT[mt] = mma32<F16>(tile_tr_operand<D>(dt, lane, ks, mt), pP[ks], dvT[mt]);
+            dkT[mt] = mma32<F16>(tile_tr_operand<D>(qt, lane, ks, mt), pS[ks], dkT[mt]);
+          }
+      }
     }
     if constexpr (kLateLoads<D>) {
       if (!active && st + 1 < nsteps) load_step(st + 1);
@@ -380,6 +413,7 @@ bwd_dkdv(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const u
 template <int D> constexpr int kQT = D == 128 ? 256 : 128;
 template <int D> constexpr int kDqThreads = 2 * kQT<D>;
 constexpr int kKB = 64;    // keys per dQ step
+
 constexpr int kPad = 128;  // row padding of the statistics workspace
 
 template <int D, bool F16>
@@ -481,15 +515,29 @@ bwd_dq(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uin
     const uint16_t *ktl = smem + (j & 1) * 2 * KTL, *vtl = ktl + KTL;
     const bool active = j0 < wave_kend;
     if (active) {
+      // S = K Q^T and dP = V dO^T for the two 32-key halves.
       f32x16 S[2], dP[2];
+      if constexpr (kOperandRing<D>) {
+        mfma_stream<4 * KST, 3>(
+            [&](auto gc) {
+              constexpr int g = decltype(gc)::value, t = g / (2 * KST), kk = (g / 2) % KST;
+              return tile_row_operand<D>(g % 2 ? vtl : ktl, lane, t, kk);
+            },
+            [&](auto gc, const uint4 &a) {
+              constexpr int g = decltype(gc)::value, t = g / (2 * KST), kk = (g / 2) % KST;
+              if constexpr (g % 2 == 0) S[t] = mma32<F16>(a, qop[kk], kk == 0 ? f32x16{} : S[t]);
+              else dP[t] = mma32<F16>(a, doop[kk], kk == 0 ? f32x16{} : dP[t]);
+            });
+      } else {
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
+        for (int t = 0; t < 2; ++t) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) S[t][r] = 0.f, dP[t][r] = 0.f;
+          for (int r = 0; r < 16; ++r) S[t][r] = 0.f, dP[t][r] = 0.f;
 #pragma unroll
-        for (int kk = 0; kk < KST; ++kk) {
-          S[t] = mma32<F16>(tile_row_operand<D>(ktl, lane, t, kk), qop[kk], S[t]);
-          dP[t] = mma32<F16>(tile_row_operand<D>(vtl, lane, t, kk), doop[kk], dP[t]);
+          for (int kk = 0; kk < KST; ++kk) {
+            S[t] = mma32<F16>(tile_row_operand<D>(ktl, lane, t, kk), qop[kk], S[t]);
+            dP[t] = mma32<F16>(tile_row_operand<D>(vtl, lane, t, kk), doop[kk], dP[t]);
+          }
         }
       }
       // Register r of tile t holds key j0 + 32 t + 16 (r / 8) + 8 hl + r % 8.
@@ -523,10 +571,22 @@ bwd_dq(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uin
       if constexpr (kLateLoads<D>) {
         if (j + 1 < nblk) load_blk(j + 1);
       }
+      if constexpr (kOperandRing<D>) {
+        mfma_stream<4 * MT, 3>(
+            [&](auto gc) {
+              constexpr int g = decltype(gc)::value;
+              return tile_tr_operand<D>(ktl, lane, g % 4, g / 4);
+            },
+            [&](auto gc, const uint4 &a) {
+              constexpr int g = decltype(gc)::value;
+              dqT[g / 4] = mma32<F16>(a, pS[g % 4], dqT[g / 4]);
+            });
+      } else {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) dqT[mt] = mma32<F16>(tile_tr_operand<D>(ktl, lane, ks, mt), pS[ks], dqT[mt]);
+          for (int ks = 0; ks < 4; ++ks) dqT[mt] = mma32<F16>(tile_tr_operand<D>(ktl, lane, ks, mt), pS[ks], dqT[mt]);
+      }
     }
     if constexpr (kLateLoads<D>) {
       if (!active && j + 1 < nblk) load_blk(j + 1);

@@ -40,15 +40,6 @@ __device__ __forceinline__ int swap_bits23(int i) {
   return (i & ~12) | ((i >> 1) & 4) | ((i << 1) & 8);
 }
 
-// f(I), f(I + 1), ..., f(N - 1) with the index a compile-time constant.
-template <int I, int N, typename F>
-__device__ __forceinline__ void static_for(F &&f) {
-  if constexpr (I < N) {
-    f(std::integral_constant<int, I>{});
-    static_for<I + 1, N>(f);
-  }
-}
-
 // Row strides (bf16 elements) of the K and V tiles in LDS. Padding replaces
 // an XOR swizzle, so every read address is a per-lane base plus a constant:
 //  - K rows of 17 (d=128) or 9 (d=64) 16-byte units: the 16 consecutive rows
