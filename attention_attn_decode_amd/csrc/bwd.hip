@@ -566,7 +566,30 @@ bwd_dq(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uin
         if (j0 + kKB - 1 < Sk && r0 + 31 < Sq && (!causal || j0 + kKB - 1 <= r0 + off)) probs(std::false_type{});
         else probs(std::true_type{});
       } else {
-        probs(std::true_type{});
+        // As in bwd_dkdv: the per-element test only where the block cuts the
+        // visible region, setting masked scores to -inf.
+        if (!(j0 + kKB - 1 < Sk && r0 + 31 < Sq && (!causal || j0 + kKB - 1 <= r0 + off))) {
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int kj = j0 + 32 * t + 16 * (r / 8) + 8 * hl + r % 8;
+              S[t][r] = kj < Sk && kj <= lim && qrow < Sq ? S[t][r] : kNegInf;
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf) {
+            float sv8[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int r = 8 * hf + e;
+              sv8[e] = exp2_hw(__builtin_fmaf(S[t][r], scale_log2, -l2)) * (dP[t][r] - Dr);
+            }
+            pS[2 * t + hf] = make_uint4(pack2<F16>(sv8[0], sv8[1]), pack2<F16>(sv8[2], sv8[3]),
+                                        pack2<F16>(sv8[4], sv8[5]), pack2<F16>(sv8[6], sv8[7]));
+          }
       }
       if constexpr (kLateLoads<D>) {
         if (j + 1 < nblk) load_blk(j + 1);
