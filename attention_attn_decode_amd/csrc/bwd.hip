@@ -340,17 +340,32 @@ bwd_dkdv(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const u
         if (kw0 + 31 < Sk && i0 + kQB - 1 < Sq && (!causal || i0 >= kw0 + 31 - off)) probs(std::false_type{});
         else probs(std::true_type{});
       } else {
+        // One copy of the loop body; only steps that cut the visible region
+        // run the per-element test, which sets masked scores to -inf (P = 0,
+        // and dS = 0 * finite: padded rows and keys read zeros). The row
+        // statistics are read per half, next to their use.
+        if (!(kw0 + 31 < Sk && i0 + kQB - 1 < Sq && (!causal || i0 >= kw0 + 31 - off))) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int qi = i0 + 16 * (r / 8) + 8 * hl + r % 8;
+            S[r] = key < Sk && qi < Sq && qi >= lim ? S[r] : kNegInf;
+          }
+        }
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
           float pv[8], sv[8];
+          const float4 la = *reinterpret_cast<const float4 *>(l2p + 16 * hf);
+          const float4 lb = *reinterpret_cast<const float4 *>(l2p + 16 * hf + 4);
+          const float4 da = *reinterpret_cast<const float4 *>(dp + 16 * hf);
+          const float4 db = *reinterpret_cast<const float4 *>(dp + 16 * hf + 4);
+          const float lh[8] = {la.x, la.y, la.z, la.w, lb.x, lb.y, lb.z, lb.w};
+          const float dh[8] = {da.x, da.y, da.z, da.w, db.x, db.y, db.z, db.w};
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const int r = 8 * hf + e;
-            const int qi = i0 + 16 * hf + 8 * hl + e;
-            const bool vis = key < Sk && qi < Sq && qi >= lim;
-            const float p = vis ? exp2_hw(__builtin_fmaf(S[r], scale_log2, -l2v[r])) : 0.f;
+            const float p = exp2_hw(__builtin_fmaf(S[r], scale_log2, -lh[e]));
             pv[e] = p;
-            sv[e] = vis ? p * (dP[r] - dv_[r]) : 0.f;
+            sv[e] = p * (dP[r] - dh[e]);
           }
           pP[hf] = make_uint4(pack2<F16>(pv[0], pv[1]), pack2<F16>(pv[2], pv[3]), pack2<F16>(pv[4], pv[5]),
                               pack2<F16>(pv[6], pv[7]));
