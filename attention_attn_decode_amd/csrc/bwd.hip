@@ -12,21 +12,24 @@
 //
 // Three kernels, no atomics and no zero-initialised memory:
 //   bwd_pre   D and L * log2(e) per query row, into the caller's workspace.
-//   bwd_dkdv  one work-group per (batch, KV head, 128-key tile), as in the
-//             page's recap: it owns its K and V rows, walks the query tiles
-//             of every query head that reads its KV head (GQA heads summed in
+//   bwd_dkdv  one work-group per (batch, KV head, key tile), as in the page's
+//             recap: it owns its K and V rows, walks the query tiles of every
+//             query head that reads its KV head (GQA heads summed in
 //             registers) and writes dK and dV once.
-//   bwd_dq    one work-group per (batch, query head, 128-row tile): it owns its
-//             Q and dO rows, walks the key tiles and writes dQ once.
+//   bwd_dq    one work-group per (batch, query head, row tile): it owns its Q
+//             and dO rows, walks the key tiles and writes dQ once.
 // The page sums dQ contributions from the KV-tile owners into an fp32 buffer
 // in global memory. Here dQ has its own pass that recomputes S and dP (seven
 // products per (query, key) tile instead of five): no atomic traffic (which
 // would be about Sk / 128 times the size of dQ), no zeroed accumulator, and
 // bitwise-reproducible results.
 //
-// Both kernels run two work-groups of four waves per CU. At d = 128 the
-// dK/dV kernel keeps its 128 V rows as a resident LDS tile (read as the dP
-// operand) instead of registers, which fits that register budget.
+// Each wave owns 32 rows (keys or queries). At d = 64 a work-group is four
+// waves (128 rows) and two run per CU; at d = 128 it is eight waves (256 rows),
+// one per CU, so each staged tile serves eight waves, and the dK/dV kernel
+// keeps its 256 V rows as a resident LDS tile (read as the dP operand)
+// instead of registers, which fits the 256-register budget of two waves per
+// SIMD. Only steps that cut the visible region run the per-element mask.
 //
 // Both main kernels use the forward's swap-AB orientation for the tile they
 // own: the owned rows (keys in bwd_dkdv, queries in bwd_dq) are the MFMA N
@@ -58,12 +61,6 @@ constexpr float kLog2e = 1.44269504088896340736f;
 // d = 128 at the top of the step (the later point raises the peak register
 // count past the two-work-groups-per-CU budget).
 template <int D> constexpr bool kLateLoads = D == 64;
-
-// A separate mask-free path for tiles wholly inside the visible region. At
-// d = 64 the per-element mask is a large share of the step's vector work (the
-// products are short); at d = 128 the second copy of the loop body pushes the
-// register count past the budget, so every tile takes the masked path.
-template <int D> constexpr bool kUnmaskedPath = D == 64;
 
 // LDS operands read three MFMAs ahead of their product through a register
 // ring (mfma_stream) at d = 64. At d = 128 the ring's registers push both
@@ -301,49 +298,13 @@ bwd_dkdv(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const u
       // Register r holds query i0 + 16 (r / 8) + 8 hl + r % 8.
       const float *l2p = &stat[st & 1][0][8 * hl];
       const float *dp = &stat[st & 1][1][8 * hl];
-      float l2v[16], dv_[16];
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-        for (int qd = 0; qd < 2; ++qd) {
-          const float4 a = *reinterpret_cast<const float4 *>(l2p + 16 * hf + 4 * qd);
-          const float4 c = *reinterpret_cast<const float4 *>(dp + 16 * hf + 4 * qd);
-          l2v[8 * hf + 4 * qd + 0] = a.x, l2v[8 * hf + 4 * qd + 1] = a.y;
-          l2v[8 * hf + 4 * qd + 2] = a.z, l2v[8 * hf + 4 * qd + 3] = a.w;
-          dv_[8 * hf + 4 * qd + 0] = c.x, dv_[8 * hf + 4 * qd + 1] = c.y;
-          dv_[8 * hf + 4 * qd + 2] = c.z, dv_[8 * hf + 4 * qd + 3] = c.w;
-        }
       const int lim = causal ? key - off : -0x40000000;  // query i sees this key iff i >= lim
       uint4 pP[2], pS[2];
-      auto probs = [&](auto masked) {  // the d = 64 form (see kUnmaskedPath)
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          float pv[8], sv[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int r = 8 * hf + e;
-            const int qi = i0 + 16 * hf + 8 * hl + e;
-            const bool vis = !decltype(masked)::value || (key < Sk && qi < Sq && qi >= lim);
-            const float p = vis ? exp2_hw(__builtin_fmaf(S[r], scale_log2, -l2v[r])) : 0.f;
-            pv[e] = p;
-            sv[e] = vis ? p * (dP[r] - dv_[r]) : 0.f;
-          }
-          pP[hf] = make_uint4(pack2<F16>(pv[0], pv[1]), pack2<F16>(pv[2], pv[3]), pack2<F16>(pv[4], pv[5]),
-                              pack2<F16>(pv[6], pv[7]));
-          pS[hf] = make_uint4(pack2<F16>(sv[0], sv[1]), pack2<F16>(sv[2], sv[3]), pack2<F16>(sv[4], sv[5]),
-                              pack2<F16>(sv[6], sv[7]));
-        }
-      };
-      // A step wholly inside the visible region (every key of the wave seen
-      // by every row, no padding) needs no mask.
-      if constexpr (kUnmaskedPath<D>) {
-        if (kw0 + 31 < Sk && i0 + kQB - 1 < Sq && (!causal || i0 >= kw0 + 31 - off)) probs(std::false_type{});
-        else probs(std::true_type{});
-      } else {
-        // One copy of the loop body; only steps that cut the visible region
-        // run the per-element test, which sets masked scores to -inf (P = 0,
-        // and dS = 0 * finite: padded rows and keys read zeros). The row
-        // statistics are read per half, next to their use.
+      {
+        // Only steps that cut the visible region (the causal diagonal, rows
+        // past Sq, keys past Sk) run the per-element test, which sets masked
+        // scores to -inf: P = 0, and dS = 0 * finite (padded rows and keys
+        // read zeros). The row statistics are read per half, next to their use.
         if (!(kw0 + 31 < Sk && i0 + kQB - 1 < Sq && (!causal || i0 >= kw0 + 31 - off))) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
@@ -557,30 +518,7 @@ bwd_dq(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uin
       }
       // Register r of tile t holds key j0 + 32 t + 16 (r / 8) + 8 hl + r % 8.
       uint4 pS[4];
-      auto probs = [&](auto masked) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int hf = 0; hf < 2; ++hf) {
-            float sv8[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const int r = 8 * hf + e;
-              const int kj = j0 + 32 * t + 16 * hf + 8 * hl + e;
-              const bool vis = !decltype(masked)::value || (kj < Sk && kj <= lim && qrow < Sq);
-              const float p = vis ? exp2_hw(__builtin_fmaf(S[t][r], scale_log2, -l2)) : 0.f;
-              sv8[e] = vis ? p * (dP[t][r] - Dr) : 0.f;
-            }
-            pS[2 * t + hf] = make_uint4(pack2<F16>(sv8[0], sv8[1]), pack2<F16>(sv8[2], sv8[3]),
-                                        pack2<F16>(sv8[4], sv8[5]), pack2<F16>(sv8[6], sv8[7]));
-          }
-      };
-      // A block wholly inside the visible region of every row of the wave
-      // needs no mask.
-      if constexpr (kUnmaskedPath<D>) {
-        if (j0 + kKB - 1 < Sk && r0 + 31 < Sq && (!causal || j0 + kKB - 1 <= r0 + off)) probs(std::false_type{});
-        else probs(std::true_type{});
-      } else {
+      {
         // As in bwd_dkdv: the per-element test only where the block cuts the
         // visible region, setting masked scores to -inf.
         if (!(j0 + kKB - 1 < Sk && r0 + 31 < Sq && (!causal || j0 + kKB - 1 <= r0 + off))) {
