@@ -315,3 +315,18 @@ def test_many_piece_merges_against_oracle(aa, case):
     assert spans <= set(K), (K, spans)
     x = wl.make_decode(len(lens), Hq, Hkv, d, sq, S, lens, seed=631 + sum(lens) % 97, pad=wl.BF16_NAN)
     check(aa, x, f"merge K={K}", num_splits=ns)
+
+
+def test_largest_batch_against_oracle(aa):
+    """batch = ATTN_MAX_BATCH (every length staged on chip), ragged lengths 0..64."""
+    rng = np.random.default_rng(651)
+    lens = rng.integers(0, 65, aa.ATTN_MAX_BATCH).astype(np.int32)
+    x = wl.make_decode(len(lens), 8, 1, 64, 1, 64, lens, seed=651, pad=wl.BF16_NAN)
+    check(aa, x, "largest batch")
+
+
+def test_million_key_sequence_against_oracle(aa):
+    """One sequence of 2^20 + 3 keys over every piece of the automatic plan."""
+    L = (1 << 20) + 3
+    x = wl.make_decode(1, 8, 1, 64, 1, L, [L], seed=653)
+    check(aa, x, "million keys")
