@@ -46,8 +46,9 @@ int check_decode_shape(int n_q_heads, int n_kv_heads, int d, int seqlen_q, int b
     return ATTN_ERR_INVALID;
   if (n_q_heads % n_kv_heads != 0) return ATTN_ERR_INVALID;
   if (batch > ATTN_MAX_BATCH || n_kv_heads > 65535) return ATTN_ERR_UNSUPPORTED;
-  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
-  if ((long)(n_q_heads / n_kv_heads) * seqlen_q > 32) return ATTN_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128 && d != 256) return ATTN_ERR_UNSUPPORTED;
+  // Packed query rows per KV head: two 16-column groups at d <= 128, one at d = 256.
+  if ((long)(n_q_heads / n_kv_heads) * seqlen_q > (d == 256 ? 16 : 32)) return ATTN_ERR_UNSUPPORTED;
   return ATTN_OK;
 }
 

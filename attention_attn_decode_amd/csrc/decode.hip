@@ -56,9 +56,11 @@ constexpr int kSliceCombine = 16;
 
 // XOR swizzle of the 16-byte chunk index of K row r in the LDS tile [32][D]:
 // the 16 rows one QK A-operand read touches land on 16 distinct bank groups.
+// At D = 256 the swizzle acts on the low four bits of the chunk index, which
+// select the bank group of a 512-byte row as of a 256-byte one.
 template <int D>
 __device__ __forceinline__ int k_swz(int r) {
-  if constexpr (D == 128) {
+  if constexpr (D >= 128) {
     return (r & 15) ^ ((r >> 4) << 2);
   } else {
     const int x = r >> 1;
@@ -72,7 +74,7 @@ __device__ __forceinline__ int k_swz(int r) {
 // chunks; this swizzle puts those 16 pieces on distinct bank groups.
 template <int D>
 __device__ __forceinline__ int v_swz(int r) {
-  if constexpr (D == 128) return 2 * ((r & 3) | (((r >> 3) & 1) << 2));
+  if constexpr (D >= 128) return 2 * ((r & 3) | (((r >> 3) & 1) << 2));
   else return 2 * (((r >> 1) & 1) | (((r >> 3) & 1) << 1));
 }
 
@@ -202,7 +204,12 @@ decode_stream(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
   constexpr int CH = S::CH, RPI = S::RPI, NK = S::NK, NVG = S::NVG, KST = S::KST;
   constexpr int MT = D / 16;
   constexpr int TILE = kSub * D;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[kWaves * 2 * TILE];
+  // At D = 256 K and V pass through one tile per wave in turn (V is written
+  // once the score MFMAs have read K), which keeps the work-group's LDS at
+  // 96 KB; below, each has its own tile.
+  constexpr bool kOneTile = D == 256;
+  constexpr int NTILE = kOneTile ? 1 : 2;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[kWaves * NTILE * TILE];
   // Clamped sequence lengths, staged once: segment walks then wait on LDS,
   // never on the vector-memory counter that the K/V stream keeps busy.
   __shared__ int lens[kMaxBatch];
@@ -236,21 +243,23 @@ decode_stream(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
   }
   const size_t rstride = (size_t)Hkv * D;
   const int slots = P + B;  // partial slots per KV head
-  uint16_t *klds = smem + wv * 2 * TILE;
-  uint16_t *vlds = klds + TILE;
+  uint16_t *klds = smem + wv * NTILE * TILE;
+  uint16_t *vlds = kOneTile ? klds : klds + TILE;
 
   // Load one sub-block (sequence b, keys [j0, j0 + 32), valid below hi) into a
   // ring slot. Rows at or past hi are clamped to hi - 1: every load is issued
   // unconditionally (a fixed count per sub-block keeps the wait counters exact)
   // and reads finite data of this sequence, which the mask then excludes.
-  auto load_slot = [&](S &sl, int b, int j0, int hi) {
+  auto load_k = [&](S &sl, int b, int j0, int hi) {
     const uint16_t *kb = kc + ((size_t)b * max_len * Hkv + g) * D;
-    const uint16_t *vb = vc + ((size_t)b * max_len * Hkv + g) * D;
 #pragma unroll
     for (int qi = 0; qi < NK; ++qi) {
       const int p = min(j0 + RPI * qi + lane / CH, hi - 1);
       sl.k[qi] = ld_stream(kb + (size_t)p * rstride + (lane % CH) * 8);
     }
+  };
+  auto load_vq = [&](S &sl, int b, int j0, int hi) {
+    const uint16_t *vb = vc + ((size_t)b * max_len * Hkv + g) * D;
 #pragma unroll
     for (int hg = 0; hg < NVG; ++hg) {
       const int g4 = lane / CH + (64 / CH) * hg;
@@ -269,6 +278,10 @@ decode_stream(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
       for (int kk = 0; kk < KST; ++kk) sl.q[c][kk] = ldg16(qrow + (4 * kk + gq) * 8);
     }
   };
+  auto load_slot = [&](S &sl, int b, int j0, int hi) {
+    load_k(sl, b, j0, hi);
+    load_vq(sl, b, j0, hi);
+  };
 
   float m_run[NC], l_run[NC];
   f32x4 oacc[NC][MT];
@@ -279,7 +292,9 @@ decode_stream(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
     for (int mt = 0; mt < MT; ++mt) oacc[c][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  auto compute_slot = [&](const S &sl, const Seg &cs, int j0, bool live) {
+  // after_k runs once K is in LDS and after_v once V is (with one tile per
+  // wave): the single-slot pipeline refills the slot's registers there.
+  auto compute_slot = [&](S &sl, const Seg &cs, int j0, bool live, auto &&after_k, auto &&after_v) {
     // K registers -> LDS (row-major, swizzled chunks).
 #pragma unroll
     for (int qi = 0; qi < NK; ++qi) {
@@ -287,16 +302,20 @@ decode_stream(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
       sts16(klds + r * D + ((c ^ k_swz<D>(r)) * 8), sl.k[qi]);
     }
     // V registers -> LDS (row-major, swizzled chunks).
+    auto store_v = [&]() {
 #pragma unroll
-    for (int hg = 0; hg < NVG; ++hg) {
-      const int g4 = lane / CH + (64 / CH) * hg, c = lane % CH;
+      for (int hg = 0; hg < NVG; ++hg) {
+        const int g4 = lane / CH + (64 / CH) * hg, c = lane % CH;
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        const int r = 4 * g4 + qq;
-        sts16(vlds + r * D + ((c ^ v_swz<D>(r)) * 8), sl.v[hg][qq]);
+        for (int qq = 0; qq < 4; ++qq) {
+          const int r = 4 * g4 + qq;
+          sts16(vlds + r * D + ((c ^ v_swz<D>(r)) * 8), sl.v[hg][qq]);
+        }
       }
-    }
+    };
+    if constexpr (!kOneTile) store_v();
     wave_lds_sync();
+    after_k();
 
     f32x4 sacc[NC][2];
 #pragma unroll
@@ -352,6 +371,12 @@ decode_stream(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
       for (int mt = 0; mt < MT; ++mt) oacc[c][mt] *= alpha;
       pop[c] = make_uint4(pack2<F16>(p[0], p[1]), pack2<F16>(p[2], p[3]), pack2<F16>(p[4], p[5]),
                           pack2<F16>(p[6], p[7]));
+    }
+    if constexpr (kOneTile) {
+      wave_lds_sync();  // every K read of the score MFMAs has returned
+      store_v();
+      wave_lds_sync();
+      after_v();
     }
     // A operand: the same eight keys 8gq .. 8gq + 7 at column 16mt + (lane % 16),
     // as two transposed 4-key reads.
@@ -413,9 +438,9 @@ decode_stream(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
   if (first.b >= B) return;
   const int n_sub = (int)(r1 - r0);  // sub-blocks of this piece
 
-  // Two ring slots, both explicit: the loads of sub-block i+2 go into slot A
-  // right after sub-block i (slot A) is consumed, while sub-block i+1 (slot B)
-  // is already in flight. Past the last sub-block the load iterator keeps
+  // Two ring slots (D <= 128), both explicit: the loads of sub-block i+2 go
+  // into slot A right after sub-block i (slot A) is consumed, while sub-block
+  // i+1 (slot B) is already in flight. Past the last sub-block the load iterator keeps
   // re-reading the last valid rows and an odd count is padded with one fully
   // masked sub-block, so the loop body has no data-dependent control flow
   // around the slots.
@@ -441,21 +466,38 @@ decode_stream(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
     }
   };
 
-  S ra, rb;
-  load_slot(ra, ls.b, lj, ls.hi);
-  advance_load();
-  load_slot(rb, ls.b, lj, ls.hi);
-  advance_load();
-  for (int i = 0; i < n_sub; i += 2) {
-    compute_slot(ra, cs, cj, true);
+  auto none = [] {};
+  if constexpr (kOneTile) {
+    // One register slot: the next sub-block's K loads are issued as soon as
+    // this one's K is in LDS, its V and Q loads once this one's V is, so they
+    // run under this sub-block's MFMAs (two slots would exceed the register
+    // file at D = 256).
+    S r;
+    load_slot(r, ls.b, lj, ls.hi);
+    advance_load();
+    for (int i = 0; i < n_sub; ++i) {
+      const int nb = ls.b, nj = lj, nhi = ls.hi;
+      compute_slot(r, cs, cj, true, [&] { load_k(r, nb, nj, nhi); }, [&] { load_vq(r, nb, nj, nhi); });
+      advance_load();
+      advance_compute();
+    }
+  } else {
+    S ra, rb;
     load_slot(ra, ls.b, lj, ls.hi);
     advance_load();
-    advance_compute();
-    const bool live_b = i + 1 < n_sub;
-    compute_slot(rb, cs, cj, live_b);
     load_slot(rb, ls.b, lj, ls.hi);
     advance_load();
-    if (live_b) advance_compute();
+    for (int i = 0; i < n_sub; i += 2) {
+      compute_slot(ra, cs, cj, true, none, none);
+      load_slot(ra, ls.b, lj, ls.hi);
+      advance_load();
+      advance_compute();
+      const bool live_b = i + 1 < n_sub;
+      compute_slot(rb, cs, cj, live_b, none, none);
+      load_slot(rb, ls.b, lj, ls.hi);
+      advance_load();
+      if (live_b) advance_compute();
+    }
   }
 }
 
@@ -689,7 +731,11 @@ hipError_t launch_decode(const void *q, const void *k, const void *v, const int3
     hipLaunchKernelGGL(kern, grid, block, 0, stream, qq, kk, vv, seqlens, oo, lse, ws_o, ws_ml, meta, batch, Hq,
                        Hkv, sq, max_len, pieces, min_units, scale_log2);
   };
-  if (d == 128) {
+  if (d == 256) {
+    // One column group only (the C ABI rejects more than 16 packed rows here).
+    if (f16) split(decode_stream<256, true, 1>);
+    else split(decode_stream<256, false, 1>);
+  } else if (d == 128) {
     if (f16) wide ? split(decode_stream<128, true, 2>) : split(decode_stream<128, true, 1>);
     else wide ? split(decode_stream<128, false, 2>) : split(decode_stream<128, false, 1>);
   } else {
@@ -707,7 +753,10 @@ hipError_t launch_decode(const void *q, const void *k, const void *v, const int3
       hipLaunchKernelGGL(kern, sgrid, dim3(256), 0, stream, ws_o, ws_ml, meta, seqlens, oo, lse, batch, Hq, Hkv,
                          sq, max_len, pieces, min_units);
     };
-    if (d == 128) {
+    if (d == 256) {
+      if (f16) slices(combine_slices<256, true, 1>);
+      else slices(combine_slices<256, false, 1>);
+    } else if (d == 128) {
       if (f16) wide ? slices(combine_slices<128, true, 2>) : slices(combine_slices<128, true, 1>);
       else wide ? slices(combine_slices<128, false, 2>) : slices(combine_slices<128, false, 1>);
     } else {
@@ -721,7 +770,10 @@ hipError_t launch_decode(const void *q, const void *k, const void *v, const int3
     hipLaunchKernelGGL(kern, cgrid, cblock, 0, stream, ws_o, ws_ml, meta, seqlens, oo, lse, batch, Hq, Hkv, sq,
                        max_len, pieces, min_units);
   };
-  if (d == 128) {
+  if (d == 256) {
+    if (f16) combine(combine_pieces<256, true, 1>);
+    else combine(combine_pieces<256, false, 1>);
+  } else if (d == 128) {
     if (f16) wide ? combine(combine_pieces<128, true, 2>) : combine(combine_pieces<128, true, 1>);
     else wide ? combine(combine_pieces<128, false, 2>) : combine(combine_pieces<128, false, 1>);
   } else {

@@ -59,7 +59,7 @@ extern "C" {
 
 #define ATTN_OK 0
 #define ATTN_ERR_INVALID (-1)     /* NULL pointer, a size <= 0, Hq % Hkv != 0, ... */
-#define ATTN_ERR_UNSUPPORTED (-2) /* d not in {64, 128}; packed query rows > 32 */
+#define ATTN_ERR_UNSUPPORTED (-2) /* head size or packed query rows out of range */
 #define ATTN_ERR_MISALIGNED (-3)  /* a data pointer not 16-byte aligned */
 #define ATTN_ERR_WORKSPACE (-4)   /* workspace smaller than the plan needs */
 #define ATTN_ERR_LAUNCH (-5)      /* the HIP runtime refused a launch */
@@ -125,10 +125,11 @@ size_t attn_decode_workspace_size(int batch, int n_q_heads, int n_kv_heads, int 
  *   lse        [batch][n_q_heads][seqlen_q] fp32 natural-log LSE, overwritten;
  *              may be NULL.
  *   The seqlen_q new tokens are causal among themselves (bottom-right mask).
- *   Requires d in {64, 128}, (n_q_heads / n_kv_heads) * seqlen_q <= 32 (the
- *   packed query rows of one KV head: one MFMA column group of 16, or two that
- *   share every K and V read) and batch <= ATTN_MAX_BATCH (else
- *   ATTN_ERR_UNSUPPORTED).
+ *   Requires d in {64, 128, 256}; (n_q_heads / n_kv_heads) * seqlen_q <= 32
+ *   at d = 64 and 128 (the packed query rows of one KV head: one MFMA column
+ *   group of 16, or two that share every K and V read) and <= 16 at d = 256
+ *   (one group: a wave streams its keys through a single register slot
+ *   there); batch <= ATTN_MAX_BATCH (else ATTN_ERR_UNSUPPORTED).
  *   workspace / workspace_bytes: caller scratch of at least
  *   attn_decode_workspace_size(...) bytes; workspace == NULL means one piece
  *   per KV head (each sequence is streamed whole by one wave; slow on few

@@ -78,6 +78,7 @@ def test_workspace_size_formula():
     # more than 16 packed rows: 32 columns per partial
     assert aa.attn_decode_workspace_size(4, 32, 1, 1, 128, 131072) == 1 * (896 + 4) * 32 * 130 * 4 + 5 * 8
     assert aa.attn_decode_workspace_size(2, 16, 2, 4, 64, 4096) == 2 * (512 + 2) * 32 * 66 * 4 + 3 * 8
+    assert aa.attn_decode_workspace_size(3, 16, 1, 1, 256, 70000) == 1 * (896 + 3) * 16 * 258 * 4 + 4 * 8
 
 
 @pytest.mark.parametrize("args,status", [
@@ -89,6 +90,11 @@ def test_workspace_size_formula():
     ((16, 1, 64, 1, 1, 64), aa.ATTN_OK),                 # G = 16, one column group
     ((32, 1, 128, 1, 1, 64), aa.ATTN_OK),                # G = 32, the widest group
     ((64, 1, 128, 1, 1, 64), aa.ATTN_ERR_UNSUPPORTED),   # G = 64
+    ((16, 1, 256, 1, 1, 64), aa.ATTN_OK),                # d = 256, 16 packed rows
+    ((8, 2, 256, 2, 1, 64), aa.ATTN_OK),                 # d = 256, G * sq = 8
+    ((32, 1, 256, 1, 1, 64), aa.ATTN_ERR_UNSUPPORTED),   # d = 256 takes one column group
+    ((32, 8, 256, 5, 1, 64), aa.ATTN_ERR_UNSUPPORTED),   # d = 256, G * sq = 20
+    ((32, 8, 192, 1, 1, 64), aa.ATTN_ERR_UNSUPPORTED),   # d = 192
     ((32, 8, 128, 0, 1, 64), aa.ATTN_ERR_INVALID),       # sq = 0
     ((32, 8, 128, 1, 0, 64), aa.ATTN_ERR_INVALID),       # batch = 0
     ((32, 8, 128, 1, 8192, 64), aa.ATTN_OK),             # largest batch

@@ -93,7 +93,7 @@ def test_bitwise_determinism(aa):
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 def test_needles_at_block_and_split_boundaries(aa, d):
     """Key j* = 8 q (score gap >> 40) must dominate: O = v[j*] for that head."""
     L, chunk_splits = 700, 33  # 13 x 700 keys in 33 pieces: piece boundaries fall inside sequences
@@ -146,7 +146,7 @@ def test_seqlens_are_clamped_to_capacity(aa):
 
 
 @pytest.mark.parametrize("shape", [(16, 1, 1), (8, 2, 4), (4, 4, 4), (1, 1, 1), (2, 1, 8), (32, 2, 1)])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 def test_group_shapes(aa, shape, d):
     """Packed query columns from 1 up to one full 16-column group, G*sq = 16 included."""
     Hq, Hkv, sq = shape
@@ -330,3 +330,27 @@ def test_million_key_sequence_against_oracle(aa):
     L = (1 << 20) + 3
     x = wl.make_decode(1, 8, 1, 64, 1, L, [L], seed=653)
     check(aa, x, "million keys")
+
+
+# Head size 256 (one column group, single register slot per wave).
+D256 = [
+    # Hq, Hkv, sq, lengths, num_splits
+    (16, 1, 1, [5000, 1, 0, 777, 33], 0),
+    (8, 2, 2, [4096, 513, 64, 65], 0),
+    (4, 4, 4, [300, 4, 3, 2000], 3),
+    (16, 2, 1, [20000], 0),             # one sequence over every piece (slice combine)
+    (8, 1, 1, [1200, 900], 1),          # one piece per KV head: no partials
+    (8, 8, 1, [3000, 2999], 4096),
+]
+
+
+@pytest.mark.parametrize("case", D256)
+def test_head_size_256_against_oracle(aa, case):
+    Hq, Hkv, sq, lens, ns = case
+    x = wl.make_decode(len(lens), Hq, Hkv, 256, sq, max(lens) + 7, lens, seed=661 + Hq + sq, pad=wl.BF16_NAN)
+    check(aa, x, f"d=256 {case}", num_splits=ns)
+
+
+def test_head_size_256_f16(aa):
+    x = wl.make_decode(3, 16, 2, 256, 1, 3000, [3000, 1234, 5], seed=671, dtype="f16")
+    check(aa, x, "d=256 f16")
