@@ -41,7 +41,7 @@ def test_status_strings_and_version():
 
 
 def _expected_pieces(Hkv, d, req):
-    n = req if req > 0 else math.ceil((896 if d == 128 else 1024) / Hkv)
+    n = req if req > 0 else math.ceil((896 if d >= 128 else 1024) / Hkv)  # 256 CUs
     return max(1, min(n, aa.ATTN_MAX_PIECES))
 
 
