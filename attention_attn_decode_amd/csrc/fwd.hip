@@ -63,12 +63,15 @@ template <int D> struct VRow { static constexpr int v = D == 128 ? 160 : 96; };
 // stages V, each during its VALU phase, one block ahead of use.
 constexpr int kBMP = 256;  // query rows per work-group
 
+// One 256-row query tile x (heaviest first: x / BH counts down the query
+// tiles, x % BH walks (sequence, head)) in the work-group's LDS block smem.
 template <int D, bool F16>
-__global__ void __launch_bounds__(512, 1)
-fwd_pp(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
-       const uint16_t *__restrict__ v, uint16_t *__restrict__ o, float *__restrict__ lse,
-       const int *__restrict__ cu_q, const int *__restrict__ cu_k, int total_q, int total_k,
-       int Sq, int Sk, int Hq, int Hkv, int causal, float scale_log2, int n_mblocks, int BH) {
+__device__ __forceinline__ void
+fwd_tile(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+         const uint16_t *__restrict__ v, uint16_t *__restrict__ o, float *__restrict__ lse,
+         const int *__restrict__ cu_q, const int *__restrict__ cu_k, int total_q, int total_k,
+         int Sq, int Sk, int Hq, int Hkv, int causal, float scale_log2, int n_mblocks, int BH, int x,
+         uint16_t *smem) {
   constexpr int BN = 64;
   constexpr int CH = D / 8;        // 16-byte chunks per row
   constexpr int KROW = KRow<D>::v, VROW = VRow<D>::v;
@@ -79,11 +82,9 @@ fwd_pp(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
   constexpr int MT = D / 32;       // O^T row tiles
   constexpr int NT = BN / 32;      // 32-key score tiles per block
   constexpr int NKS = BN / 16;     // 16-key P*V steps per block
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (KT + VT)];
   uint16_t *const ktile = smem;           // K slots 0, 1
   uint16_t *const vtile = smem + 2 * KT;  // V slots 0, 1
 
-  const int x = blockIdx.x;
   const int mb = n_mblocks - 1 - x / BH;  // heaviest query tile first
   const int u = x % BH;
   const int b = u / Hq, h = u % Hq;
@@ -372,6 +373,51 @@ fwd_pp(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     lse[lse_base + (size_t)h * lse_hs + qrow] = l_col > 0.f ? kLn2 * (m_run + __log2f(l_col)) : kNegInf;
 }
 
+
+template <int D> constexpr int kTileLds = 2 * 64 * (KRow<D>::v + VRow<D>::v);  // elements
+// Waves per SIMD: two (one work-group per CU) at d = 128, four at d = 64,
+// where the kernel fits in 128 registers and two work-groups share a CU.
+template <int D> constexpr int kPrefillWaves = D == 64 ? 4 : 2;
+
+// One work-group per query tile, dispatched heaviest first.
+template <int D, bool F16>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(kPrefillWaves<D>, kPrefillWaves<D>)))
+fwd_pp(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+       const uint16_t *__restrict__ v, uint16_t *__restrict__ o, float *__restrict__ lse,
+       const int *__restrict__ cu_q, const int *__restrict__ cu_k, int total_q, int total_k,
+       int Sq, int Sk, int Hq, int Hkv, int causal, float scale_log2, int n_mblocks, int BH) {
+  __shared__ __attribute__((aligned(16))) uint16_t smem[kTileLds<D>];
+  fwd_tile<D, F16>(q, k, v, o, lse, cu_q, cu_k, total_q, total_k, Sq, Sk, Hq, Hkv, causal, scale_log2, n_mblocks, BH,
+                   blockIdx.x, smem);
+}
+
+// Persistent form ([FA4-edges] §Edge 3, tile scheduling): one resident
+// work-group per CU walks the heaviest-first tile list in rounds of gridDim.x
+// tiles, in snake order (forward in even rounds, backward in odd ones), so
+// the heavy and light ends of consecutive rounds pair up on each CU. The
+// assignment is static: no counter, nothing to clear between calls. The
+// launcher takes it for dense batches at d = 128; a packed batch's empty
+// tiles would unbalance a static assignment, and at d = 64 two dispatched
+// work-groups per CU are faster.
+template <int D, bool F16>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+fwd_persist(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+            const uint16_t *__restrict__ v, uint16_t *__restrict__ o, float *__restrict__ lse,
+            const int *__restrict__ cu_q, const int *__restrict__ cu_k, int total_q, int total_k,
+            int Sq, int Sk, int Hq, int Hkv, int causal, float scale_log2, int n_mblocks, int BH) {
+  __shared__ __attribute__((aligned(16))) uint16_t smem[kTileLds<D>];
+  const long long ntiles = (long long)n_mblocks * BH;
+  const int G = gridDim.x, g = blockIdx.x;
+  bool odd = false;
+  for (long long base = 0; base < ntiles; base += G, odd = !odd) {
+    const long long x = base + (odd ? G - 1 - g : g);
+    if (x < ntiles)
+      fwd_tile<D, F16>(q, k, v, o, lse, cu_q, cu_k, total_q, total_k, Sq, Sk, Hq, Hkv, causal, scale_log2, n_mblocks,
+                       BH, (int)x, smem);
+    __syncthreads();  // the next tile's prologue rewrites the LDS slots
+  }
+}
+
 }  // namespace
 
 // Dense when cu_q == nullptr (Sq, Sk the per-sequence lengths); packed
@@ -382,21 +428,30 @@ hipError_t launch_fwd(const void *q, const void *k, const void *v, void *o, floa
                       int Hkv, int d, float scale_log2, bool f16, hipStream_t stream) {
   const int BH = batch * Hq;
   const int n_mblocks = (Sq + kBMP - 1) / kBMP;
-  const dim3 grid(n_mblocks * BH), block(512);
+  const int ntiles = n_mblocks * BH;
+  const dim3 block(512);
   const auto *qq = static_cast<const uint16_t *>(q);
   const auto *kk = static_cast<const uint16_t *>(k);
   const auto *vv = static_cast<const uint16_t *>(v);
   auto *oo = static_cast<uint16_t *>(o);
-  auto run = [&](auto kern) {
-    hipLaunchKernelGGL(kern, grid, block, 0, stream, qq, kk, vv, oo, lse, cu_q, cu_k, total_q, total_k, Sq, Sk, Hq,
-                       Hkv, causal, scale_log2, n_mblocks, BH);
+  auto run = [&](auto kern, int nwg) {
+    hipLaunchKernelGGL(kern, dim3(nwg), block, 0, stream, qq, kk, vv, oo, lse, cu_q, cu_k, total_q, total_k, Sq, Sk,
+                       Hq, Hkv, causal, scale_log2, n_mblocks, BH);
   };
-  if (d == 128) {
-    if (f16) run(fwd_pp<128, true>);
-    else run(fwd_pp<128, false>);
+  if (d == 128 && cu_q == nullptr) {
+    int dev = 0, ncu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0)
+      return hipErrorInvalidDevice;
+    const int nwg = ntiles < ncu ? ntiles : ncu;
+    if (f16) run(fwd_persist<128, true>, nwg);
+    else run(fwd_persist<128, false>, nwg);
+  } else if (d == 128) {
+    if (f16) run(fwd_pp<128, true>, ntiles);
+    else run(fwd_pp<128, false>, ntiles);
   } else {
-    if (f16) run(fwd_pp<64, true>);
-    else run(fwd_pp<64, false>);
+    if (f16) run(fwd_pp<64, true>, ntiles);
+    else run(fwd_pp<64, false>, ntiles);
   }
   return hipGetLastError();
 }

@@ -89,7 +89,7 @@ COPY_BYTES = 1 << 30
 TRAFFIC_KERNELS = {  # stored key -> (kernel-name prefixes, sources, workload)
     "attn_decode": (("decode_stream<", "combine_pieces<"), DECODE_SOURCES,
                     "gqa-decode b=32 hq=64 hkv=8 d=128 sq=1 kv_len~U[1024,8192] (seed 1001)"),
-    "fwd_pp": (("fwd_pp<",), FWD_SOURCES, "causal-prefill b=2 h=32 d=128 s=8192 (seed 1004)"),
+    "attn_fwd": (("fwd_persist<", "fwd_pp<"), FWD_SOURCES, "causal-prefill b=2 h=32 d=128 s=8192 (seed 1004)"),
     "attn_bwd": (("bwd_pre<", "bwd_dkdv<", "bwd_dq<"), BWD_SOURCES,
                  "causal-prefill backward b=2 h=32 d=128 s=8192 (seed 1004, dO seed 1005)"),
 }
@@ -382,7 +382,7 @@ def main():
         tf = fl / (pre_mean * 1e-3) / 1e12
         result["prefill"] = {
             "bound": "mfma",
-            "kernel": "fwd_pp",
+            "kernel": "fwd_persist (dense d = 128: one persistent work-group per CU)",
             "ms_mean": round(pre_mean, 5),
             "ms_median": round(statistics.median(pre_ms), 5),
             "flops": fl,
@@ -390,7 +390,7 @@ def main():
             "peak": BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(tf / BF16_PEAK_TFLOPS, 4),
-            "traffic": measured_traffic("fwd_pp", source_hash(FWD_SOURCES), None),
+            "traffic": measured_traffic("attn_fwd", source_hash(FWD_SOURCES), None),
         }
     if run_backward:
         bwd_mean = statistics.fmean(bwd_ms)
@@ -416,7 +416,7 @@ def main():
         tf = fl / (var_mean * 1e-3) / 1e12
         result["varlen_prefill"] = {
             "bound": "mfma",
-            "kernel": "fwd_pp (packed offsets)",
+            "kernel": "fwd_pp (packed offsets, one work-group per tile)",
             "ms_mean": round(var_mean, 5),
             "ms_median": round(statistics.median(var_ms), 5),
             "tokens": int(lens_v.sum()),

@@ -68,6 +68,28 @@ def test_varlen_equal_lengths_bitwise_equal_dense(aa):
     assert np.array_equal(lse, G.host_f64(ld).transpose(1, 0, 2).reshape(Hq, B * S))
 
 
+@pytest.mark.parametrize("causal", [True, False])
+def test_dense_tile_rounds_bitwise_equal_packed(aa, causal):
+    """356 query tiles of 256 rows (B=2, S=22784, 2 heads) are more than one
+    round of resident work-groups, and the second (reversed) round is partial:
+    the dense d = 128 call, which walks the tile list in rounds, must write
+    every row exactly as the packed call, which dispatches one work-group per
+    tile, does (outputs start as NaN, so a skipped tile shows)."""
+    torch = G.torch()
+    B, S, Hq, Hkv, d = 2, 89 * 256, 2, 1, 128
+    x = wl.make_varlen([S] * B, [S] * B, Hq, Hkv, d, seed=741)
+    o, lse = run_varlen(aa, x, causal)
+    qd = G.dev_bf16(x.q.reshape(B, S, Hq, d))
+    kd, vd = G.dev_bf16(x.k.reshape(B, S, Hkv, d)), G.dev_bf16(x.v.reshape(B, S, Hkv, d))
+    od = G.nan_like_bf16(qd.shape)
+    ld = G.nan_f32((B, Hq, S))
+    aa.attn_fwd(qd, kd, vd, od, ld, causal=causal)
+    torch.cuda.synchronize()
+    assert not np.isnan(o).any()
+    assert np.array_equal(o, G.host_f64(od).reshape(B * S, Hq, d))
+    assert np.array_equal(lse, G.host_f64(ld).transpose(1, 0, 2).reshape(Hq, B * S))
+
+
 def test_varlen_larger_max_seqlen_changes_nothing(aa):
     x = wl.make_varlen([300, 20], [300, 20], 2, 2, 64, seed=721)
     a = run_varlen(aa, x, True)
