@@ -109,10 +109,24 @@ __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcn
 // c0 + 4 (k % 4) .. +3 of a row-major tile, lane i therefore receives column
 // c0 + i of rows R(0..3): a 4 x 16 block comes back transposed, one column per
 // lane, which is the k-major operand layout the MFMAs take.
+// LDS reads at a byte address within the work-group's LDS allocation.
+__device__ __forceinline__ uint4 lds16_at(unsigned a) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  return __builtin_bit_cast(uint4, *(const u32x4 __attribute__((address_space(3))) *)(uintptr_t)a);
+}
+__device__ __forceinline__ unsigned lds_offset(const void *p) { return (unsigned)reinterpret_cast<uintptr_t>(p); }
+
 __device__ __forceinline__ uint2 lds_tr4(const uint16_t *p) {
   typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
   const bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
       (bf16x4 __attribute__((address_space(3))) *)(reinterpret_cast<uintptr_t>(p)));
+  return __builtin_bit_cast(uint2, v);
+}
+
+// lds_tr4 at an LDS byte address.
+__device__ __forceinline__ uint2 lds_tr4_at(unsigned a) {
+  typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+  const bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4 __attribute__((address_space(3))) *)(uintptr_t)a);
   return __builtin_bit_cast(uint2, v);
 }
 

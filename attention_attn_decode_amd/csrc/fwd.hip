@@ -52,15 +52,16 @@ template <int D> struct VRow { static constexpr int v = D == 128 ? 160 : 96; };
 // Ping-pong schedule. A work-group of eight waves covers 256 query rows; waves
 // 0-3 form group A and waves 4-7 group B, so every SIMD holds one wave of each.
 // Each wave owns 32 query columns and alternates two phases per key block j:
-//   MFMA phase j: O^T += V(j-1)^T P(j-1)^T, then S(j) = K(j) Q^T (32 MFMAs)
-//   VALU phase j: softmax of S(j) into P(j), the rescale of O^T, and the
-//                 group's share of the K/V staging.
+//   MFMA phase j: O^T += V(j-1)^T P(j-1)^T, then S(j) = K(j) Q^T (32 MFMAs),
+//                 with the group's share of the K/V staging under them
+//   VALU phase j: softmax of S(j) into P(j) and the rescale of O^T.
 // Group B runs one phase behind group A and every phase ends in a work-group
 // barrier, so on each SIMD one wave issues MFMAs while the other runs its
 // exponentials: the S/P ping-pong of [FA4-decode] §Recap on the FA4 forward
 // pass, played between the two waves of a SIMD instead of two register sets.
 // K and V tiles are shared by all eight waves; group A stages K, group B
-// stages V, each during its VALU phase, one block ahead of use.
+// stages V, each during its MFMA phase, ahead of use (one block through
+// registers at d = 64, two half-steps by direct-to-LDS loads at d = 128).
 constexpr int kBMP = 256;  // query rows per work-group
 
 // One 256-row query tile x (heaviest first: x / BH counts down the query
@@ -74,7 +75,12 @@ fwd_tile(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
          uint16_t *smem) {
   constexpr int BN = 64;
   constexpr int CH = D / 8;        // 16-byte chunks per row
-  constexpr int KROW = KRow<D>::v, VROW = VRow<D>::v;
+  // d = 128: K/V staged by direct-to-LDS buffer loads into three slots of
+  // dense, chunk-swizzled rows; d = 64: through registers into two slots of
+  // padded rows.
+  constexpr bool kDma = D == 128;
+  constexpr int NSLOT = kDma ? 3 : 2;
+  constexpr int KROW = kDma ? D : KRow<D>::v, VROW = kDma ? D : VRow<D>::v;
   constexpr int KT = BN * KROW, VT = BN * VROW;
   constexpr int RPT = 256 / CH;    // rows one group-wide (256-thread) load covers
   constexpr int NKL = BN / RPT;    // tile loads per thread per block
@@ -82,8 +88,8 @@ fwd_tile(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
   constexpr int MT = D / 32;       // O^T row tiles
   constexpr int NT = BN / 32;      // 32-key score tiles per block
   constexpr int NKS = BN / 16;     // 16-key P*V steps per block
-  uint16_t *const ktile = smem;           // K slots 0, 1
-  uint16_t *const vtile = smem + 2 * KT;  // V slots 0, 1
+  uint16_t *const ktile = smem;               // K slots
+  uint16_t *const vtile = smem + NSLOT * KT;  // V slots
 
   const int mb = n_mblocks - 1 - x / BH;  // heaviest query tile first
   const int u = x % BH;
@@ -149,27 +155,96 @@ fwd_tile(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
   const int drow = G == 0 ? KROW : VROW, dsize = G == 0 ? KT : VT;
   const int tg = tid & 255, trow = tg / CH, tcol = (tg % CH) * 8;
   const int voff = (int)((trow * rstride + tcol) * 2);
-  uint4 sreg[NKL];
-  auto load_blk = [&](int blk) {
+  auto slot_of = [](int blk) { return kDma ? blk % 3 : blk & 1; };
+  auto rsrc_blk = [&](int blk) {
     const long long boff = (long long)blk * BN * (long long)rstride * 2;
     const long long left = src_bytes - boff;
     const int nrec = left <= 0 ? 0 : (left > 0x7fffffffLL ? 0x7fffffff : (int)left);
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+    return __builtin_amdgcn_make_buffer_rsrc(
         (void *)(reinterpret_cast<const char *>(src) + (left <= 0 ? 0 : boff)), (short)0, nrec, kBufferWord3);
+  };
+  uint4 sreg[kDma ? 1 : NKL];
+  auto load_blk = [&](int blk) {
+    const __amdgpu_buffer_rsrc_t rs = rsrc_blk(blk);
 #pragma unroll
     for (int qi = 0; qi < NKL; ++qi)
       sreg[qi] = __builtin_bit_cast(
           uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff + (int)(qi * RPT * rstride * 2), 0, 0));
   };
   auto store_blk = [&](int blk) {
-    uint16_t *dst = dtile + (blk & 1) * dsize + trow * drow + tcol;
+    uint16_t *dst = dtile + slot_of(blk) * dsize + trow * drow + tcol;
 #pragma unroll
     for (int qi = 0; qi < NKL; ++qi) sts16(dst + RPT * qi * drow, sreg[qi]);
   };
+  // Direct-to-LDS staging (d = 128): each wave of a group moves 16 rows of
+  // the block with four buffer loads whose 64 lanes deposit 16 bytes each,
+  // in lane order, at the LDS address in M0 (four dense 256-byte rows per
+  // load). Lane l of load i therefore fetches the chunk that the swizzle
+  // places at chunk l % 16 of row 4i + l / 16. All offsets are per lane, so
+  // the descriptor's range check zeroes rows past Sk. The compiler does not
+  // see these writes: the waits that publish a slot are explicit. A load
+  // that takes its LDS address from M0 needs one wait state after M0 is set.
+  constexpr int RPI = 64 / CH;  // rows per load
+  constexpr int NI = 16 / RPI;  // loads per wave per block
+  const int w4 = w & 3;
+  int dvoff[kDma ? NI : 1];
+  if constexpr (kDma) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int rw = 16 * w4 + RPI * i + lane / CH;
+      dvoff[i] = (int)((rw * rstride + 8 * ((lane % CH) ^ chunk_swz<D>(rw))) * 2);
+    }
+  }
+  const unsigned lds_wave = lds_offset(dtile) + (unsigned)(16 * w4 * D * 2);
+  auto dma_blk = [&](int blk) {
+    const __amdgpu_buffer_rsrc_t rs = rsrc_blk(blk);
+    const unsigned slotb = lds_wave + (unsigned)(slot_of(blk) * dsize * 2);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const unsigned la = __builtin_amdgcn_readfirstlane(slotb + RPI * i * D * 2);
+      // M0 is listed as clobbered; the compiler warns because it reserves
+      // M0, and this kernel leaves M0 to these loads alone.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+      asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(dvoff[i]), "s"(rs), "s"(la)
+                   : "memory", "m0");
+#pragma clang diagnostic pop
+    }
+  };
+  // Wait until at most one block's direct loads (the newest) are in flight.
+  auto dma_wait_one = [&]() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NI) : "memory"); };
 
-  const int k_lane = swap_bits23(n) * KROW + hl * 8;
+  // Operand reads. Padded rows (d = 64): a lane base plus constants.
+  // Swizzled rows (d = 128): chunk c of row r sits at chunk c ^ chunk_swz(r);
+  // the rows one lane reads share their swizzle up to compile-time terms, so
+  // each address is a lane base XOR a constant, plus a constant.
+  const int pin = swap_bits23(n);
+  const int k_lane = pin * KROW + hl * 8;
   const int trk = lane & 15, trhalf = (lane >> 4) & 1;
   const int v_lane = (8 * hl + (trk >> 2)) * VROW + 16 * trhalf + 4 * (trk & 3);
+  const unsigned k_lane_b = lds_offset(ktile) + pin * D * 2 + 16 * (hl ^ chunk_swz<D>(pin));
+  const unsigned v_lane_b = lds_offset(vtile) + (8 * hl + (trk >> 2)) * D * 2 +
+                            16 * (((2 * trhalf + ((trk & 3) >> 1)) ^ (2 * hl)) | ((trk >> 2) << 2)) + 8 * (trk & 1);
+  // K rows 32t + pi(n), 16-byte chunk 2kk + hl.
+  auto kread = [&](int slot, int t, int kk) {
+    if constexpr (kDma) return lds16_at(((k_lane_b + slot * KT * 2) ^ (kk << 5)) + t * 32 * D * 2);
+    else return lds16(ktile + slot * KT + k_lane + 32 * t * KROW + 16 * kk);
+  };
+  // V^T operand of 16-key step ks and O^T row tile mt (two transposing reads
+  // of rows 16ks + 8hl + trk/4 and 4 rows further).
+  auto vread = [&](int slot, int ks, int mt) {
+    uint2 t0, t1;
+    if constexpr (kDma) {
+      const unsigned bb = v_lane_b + slot * VT * 2;
+      t0 = lds_tr4_at((bb ^ (mt << 6)) + 16 * ks * D * 2);
+      t1 = lds_tr4_at((bb ^ ((mt << 6) | 16)) + (16 * ks + 4) * D * 2);
+    } else {
+      const uint16_t *vl = vtile + slot * VT + v_lane;
+      t0 = lds_tr4(vl + 16 * ks * VROW + 32 * mt);
+      t1 = lds_tr4(vl + (16 * ks + 4) * VROW + 32 * mt);
+    }
+    return make_uint4(t0.x, t0.y, t1.x, t1.y);
+  };
 
   f32x16 S[NT];
   uint4 pop[NKS];
@@ -181,25 +256,19 @@ fwd_tile(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     for (int r = 0; r < 16; ++r) oacc[mt][r] = 0.f;
 
   auto qk = [&](int slot) {
-    const uint16_t *kl = ktile + slot * KT + k_lane;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) S[t][r] = 0.f;
 #pragma unroll
-      for (int kk = 0; kk < KST; ++kk) S[t] = mma32<F16>(lds16(kl + 32 * t * KROW + 16 * kk), qop[kk], S[t]);
+      for (int kk = 0; kk < KST; ++kk) S[t] = mma32<F16>(kread(slot, t, kk), qop[kk], S[t]);
     }
   };
   auto pv = [&](int slot) {
-    const uint16_t *vl = vtile + slot * VT + v_lane;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const uint2 t0 = lds_tr4(vl + 16 * ks * VROW + 32 * mt);
-        const uint2 t1 = lds_tr4(vl + (16 * ks + 4) * VROW + 32 * mt);
-        oacc[mt] = mma32<F16>(make_uint4(t0.x, t0.y, t1.x, t1.y), pop[ks], oacc[mt]);
-      }
+      for (int ks = 0; ks < NKS; ++ks) oacc[mt] = mma32<F16>(vread(slot, ks, mt), pop[ks], oacc[mt]);
   };
   // Softmax of block j0 (register r of score tile t holds key
   // j0 + 32t + 16(r/8) + 8hl + (r%8)) into the bf16 P operands, with the
@@ -255,17 +324,10 @@ fwd_tile(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
   constexpr int KDEP = 3;
   static_assert(NPV == NT * KST, "both products have the same MFMA count");
   auto pv_qk = [&](int vslot, int kslot, int j) {
-    const uint16_t *vl = vtile + vslot * VT + v_lane;
-    const uint16_t *kl = ktile + kslot * KT + k_lane;
     auto rd = [&](int g) {
-      if (g < NPV) {
-        const int ks = g / MT, mt = g % MT;
-        const uint2 t0 = lds_tr4(vl + 16 * ks * VROW + 32 * mt);
-        const uint2 t1 = lds_tr4(vl + (16 * ks + 4) * VROW + 32 * mt);
-        return make_uint4(t0.x, t0.y, t1.x, t1.y);
-      }
+      if (g < NPV) return vread(vslot, g / MT, g % MT);
       const int m = g - NPV;
-      return lds16(kl + 32 * (m % NT) * KROW + 16 * (m / NT));
+      return kread(kslot, m % NT, m / NT);
     };
     uint4 ring[KDEP];
 #pragma unroll
@@ -277,8 +339,12 @@ fwd_tile(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
       // This group's share of the staging (see stage below), unconditional in
       // the steady range: a block past the work-group's last is loaded (rows
       // past Sk as zeros) into a slot nobody reads again.
-      if constexpr (g == 2) store_blk(j + 1 - G);
-      if constexpr (g == 6) load_blk(j + 2 - G);
+      if constexpr (kDma) {
+        if constexpr (g == 2) dma_blk(j + 2 - G);
+      } else {
+        if constexpr (g == 2) store_blk(j + 1 - G);
+        if constexpr (g == 6) load_blk(j + 2 - G);
+      }
       if constexpr (g < NPV) {
         constexpr int ks = g / MT, mt = g % MT;
         oacc[mt] = mma32<F16>(a, pop[ks], oacc[mt]);
@@ -295,15 +361,24 @@ fwd_tile(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
   // last read in the previous half-step) and loads K(j+2); group B, half a
   // step later, writes V(j) (into V(j-2)'s slot) and loads V(j+1). Each tile
   // is visible one barrier before its first reader.
+  // With direct loads (three slots), group A loads K(j+2) in its phase j
+  // into the slot K(j-1) held, last read in the previous half-step, and group
+  // B loads V(j+1) into the slot of V(j-2): two half-steps of lead. A block
+  // past the last loads zeros into a slot nobody reads again.
   auto stage = [&](int j) {
-    if (j + 1 - G < nblk) store_blk(j + 1 - G);
-    if (j + 2 - G < nblk) load_blk(j + 2 - G);
+    if constexpr (kDma) {
+      if (G == 0 && j == 0) dma_blk(1);
+      dma_blk(j + 2 - G);
+    } else {
+      if (j + 1 - G < nblk) store_blk(j + 1 - G);
+      if (j + 2 - G < nblk) load_blk(j + 2 - G);
+    }
   };
   auto mfma_phase = [&](int j) {
     __builtin_amdgcn_s_setprio(2);
     stage(j);
-    if (j >= 1 && j - 1 < nbw) pv((j - 1) & 1);
-    if (j < nbw) qk(j & 1);
+    if (j >= 1 && j - 1 < nbw) pv(slot_of(j - 1));
+    if (j < nbw) qk(slot_of(j));
     __builtin_amdgcn_s_setprio(0);
   };
   auto valu_phase = [&](int j) {
@@ -313,8 +388,13 @@ fwd_tile(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     }
   };
 
-  // Prologue: K(0) into slot 0; group A holds K(1), group B V(0) in registers.
-  if (nblk > 0) {
+  // Prologue. Register staging: K(0) into slot 0; group A holds K(1), group B
+  // V(0) in registers. Direct loads: K(0) and V(0) into slot 0, then a wait
+  // the compiler sees, so none of its own loads (Q) is pending in the loops.
+  if constexpr (kDma) {
+    dma_blk(0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  } else if (nblk > 0) {
     if (G == 0) {
       load_blk(0);
       store_blk(0);
@@ -332,8 +412,10 @@ fwd_tile(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
   int j = 0;
   for (; j <= nblk && (j == 0 || j >= nbw); ++j) {  // j = 0, or a wave with nbw <= 1
     mfma_phase(j);
+    if (kDma && G == 1) dma_wait_one();
     __syncthreads();
     valu_phase(j);
+    if (kDma && G == 0) dma_wait_one();
     __syncthreads();
     if (j == 0 && nbw > 1) {
       ++j;
@@ -342,18 +424,25 @@ fwd_tile(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
   }
   for (; j < nbw; ++j) {
     __builtin_amdgcn_s_setprio(2);
-    pv_qk((j - 1) & 1, j & 1, j);
+    pv_qk(slot_of(j - 1), slot_of(j), j);
     __builtin_amdgcn_s_setprio(0);
+    if (kDma && G == 1) dma_wait_one();
     __syncthreads();
     valu_phase(j);
+    if (kDma && G == 0) dma_wait_one();
     __syncthreads();
   }
   for (; j <= nblk; ++j) {
     mfma_phase(j);
+    if (kDma && G == 1) dma_wait_one();
     __syncthreads();
     valu_phase(j);
+    if (kDma && G == 0) dma_wait_one();
     __syncthreads();
   }
+  // Direct loads still in flight (zeros past the last block) land before
+  // the slots are reused.
+  if constexpr (kDma) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   if (G == 0) __syncthreads();
 
   const float l_col = wave_xor_sum(l_run, 32);
@@ -374,7 +463,7 @@ fwd_tile(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
 }
 
 
-template <int D> constexpr int kTileLds = 2 * 64 * (KRow<D>::v + VRow<D>::v);  // elements
+template <int D> constexpr int kTileLds = D == 128 ? 3 * 2 * 64 * D : 2 * 64 * (KRow<D>::v + VRow<D>::v);  // elements
 // Waves per SIMD: two (one work-group per CU) at d = 128, four at d = 64,
 // where the kernel fits in 128 registers and two work-groups share a CU.
 template <int D> constexpr int kPrefillWaves = D == 64 ? 4 : 2;
