@@ -169,7 +169,12 @@ int attn_decode_f16(const void *q, const void *k_cache, const void *v_cache,
  * [batch][n_q_heads][seqlen_q] fp32 (may be NULL). causal != 0 applies the
  * bottom-right mask (query i sees keys j <= i + seqlen_k - seqlen_q).
  * Requires d == 128 or d == 64. Work-groups of eight waves own 256 query rows
- * and are launched heaviest first (longest visible key range first).
+ * and take them heaviest first (longest visible key range first): at d = 128
+ * one persistent work-group per compute unit walks the tile list in rounds
+ * (the CU count is read from the current device; ATTN_ERR_LAUNCH if it cannot
+ * be), at d = 64 one work-group is launched per tile. The tile order does not
+ * change the result: each row's output is computed by one wave in a fixed
+ * order.
  */
 int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int causal,
              int batch, int seqlen_q, int seqlen_k, int n_q_heads, int n_kv_heads, int d,
@@ -195,9 +200,11 @@ int attn_fwd_f16(const void *q, const void *k, const void *v, void *o, float *ls
  *   max_seqlen_q  at least the longest query length: it sizes the grid, and
  *          query rows past it are not computed.
  * A sequence with no keys gets O = 0 and LSE = -inf. Requires d == 64 or
- * d == 128 and total_q >= 1. Same kernel as attn_fwd, one work-group per
- * (256-row query tile, sequence, query head), longest tile index first; a
- * work-group past its sequence's last tile exits at once.
+ * d == 128 and total_q >= 1. Same tile code as attn_fwd, always one
+ * work-group per (256-row query tile, sequence, query head), longest tile
+ * index first; a work-group past its sequence's last tile exits at once (a
+ * static persistent assignment would not see the lengths, which live on the
+ * device).
  */
 int attn_fwd_varlen(const void *q, const void *k, const void *v, const int32_t *cu_seqlens_q,
                     const int32_t *cu_seqlens_k, void *o, float *lse, int causal, int batch,
