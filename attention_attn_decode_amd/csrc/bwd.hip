@@ -270,6 +270,10 @@ bwd_dkdv(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const u
     // Skip when every query of the step is before the wave's first visible one.
     const bool active = i0 + kQB - 1 >= wave_first_i && kw0 < Sk;
     if (active) {
+      // The two waves of a SIMD share its matrix unit: a wave issuing MFMAs
+      // runs at raised priority, so the other's softmax work fills the gaps
+      // instead of competing with it.
+      __builtin_amdgcn_s_setprio(2);
       f32x16 S, dP;
       if constexpr (kOperandRing<D> && !kVinLds) {
         // S^T = K Q^T and dP^T = V dO^T as one stream (Q and dO rows from LDS).
@@ -295,6 +299,7 @@ bwd_dkdv(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const u
           dP = mma32<F16>(tile_row_operand<D>(dt, lane, 0, kk), vb, dP);
         }
       }
+      __builtin_amdgcn_s_setprio(0);
       // Register r holds query i0 + 16 (r / 8) + 8 hl + r % 8.
       const float *l2p = &stat[st & 1][0][8 * hl];
       const float *dp = &stat[st & 1][1][8 * hl];
@@ -337,6 +342,7 @@ bwd_dkdv(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const u
       if constexpr (kLateLoads<D>) {
         if (st + 1 < nsteps) load_step(st + 1);
       }
+      __builtin_amdgcn_s_setprio(2);
       if constexpr (kOperandRing<D>) {
         // dV^T += dO^T P^T and dK^T += Q^T dS^T as one stream.
         mfma_stream<4 * MT, 3>(
@@ -359,6 +365,7 @@ bwd_dkdv(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const u
           }
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     if constexpr (kLateLoads<D>) {
       if (!active && st + 1 < nsteps) load_step(st + 1);
     }
@@ -491,6 +498,7 @@ bwd_dq(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uin
     const uint16_t *ktl = smem + (j & 1) * 2 * KTL, *vtl = ktl + KTL;
     const bool active = j0 < wave_kend;
     if (active) {
+      __builtin_amdgcn_s_setprio(2);
       // S = K Q^T and dP = V dO^T for the two 32-key halves.
       f32x16 S[2], dP[2];
       if constexpr (kOperandRing<D>) {
@@ -516,6 +524,7 @@ bwd_dq(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uin
           }
         }
       }
+      __builtin_amdgcn_s_setprio(0);
       // Register r of tile t holds key j0 + 32 t + 16 (r / 8) + 8 hl + r % 8.
       uint4 pS[4];
       {
@@ -547,6 +556,7 @@ bwd_dq(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uin
       if constexpr (kLateLoads<D>) {
         if (j + 1 < nblk) load_blk(j + 1);
       }
+      __builtin_amdgcn_s_setprio(2);
       if constexpr (kOperandRing<D>) {
         mfma_stream<4 * MT, 3>(
             [&](auto gc) {
@@ -564,6 +574,7 @@ bwd_dq(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uin
           for (int ks = 0; ks < 4; ++ks) dqT[mt] = mma32<F16>(tile_tr_operand<D>(ktl, lane, ks, mt), pS[ks], dqT[mt]);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     if constexpr (kLateLoads<D>) {
       if (!active && j + 1 < nblk) load_blk(j + 1);
     }
