@@ -44,6 +44,10 @@ def run_fwd(aa, x, causal=True):
     (2, 64, 1000, 4, 4, 64, False),
     (1, 1, 1, 1, 1, 128, True),
     (1, 513, 513, 3, 1, 128, True),
+    (1, 40, 40, 2, 2, 128, True),       # one partial key block
+    (1, 70, 1, 2, 1, 128, True),        # a single key: only the last row sees it
+    (1, 1, 700, 2, 2, 128, True),       # one query row over a ragged key range
+    (2, 333, 191, 4, 2, 128, False),    # ragged both ways, GQA, non-causal
 ])
 def test_fwd_small_shapes(aa, shape):
     B, Sq, Sk, Hq, Hkv, d, causal = shape
@@ -84,6 +88,31 @@ def test_fwd_causal_prefill_workload_sampled(aa):
     print(f"[fwd parity] c5 sampled {len(rows)} rows: max|dO| = {err:.3e}", flush=True)
     # property at any size: O rows are convex combinations of V rows -> |O| <= max|V| per column
     assert np.abs(o).max() <= np.abs(oracle.bf16_bits_to_f64(x.v)).max() + 1e-2
+
+
+def test_fwd_tile_rounds_ragged_gqa_sampled(aa):
+    """868 query tiles (62 of 256 rows x 14 heads): three full rounds of resident
+    work-groups and a partial reversed fourth, ragged Sq = 15653 < Sk = 15700
+    (bottom-right causal), 7 query heads per KV head; oracle on sampled rows,
+    among them each round's first and last tiles and the ragged ends."""
+    B, Sq, Sk, Hq, Hkv, d = 1, 15653, 15700, 14, 2, 128
+    x = wl.make_prefill(B, Hq, Hkv, d, Sq, Sk, seed=97)
+    print(f"[fwd parity] rounds shape q {x.q.shape} k {x.k.shape}", flush=True)
+    o, lse = run_fwd(aa, x, True)
+    rng = np.random.default_rng(9)
+    rows = set()
+    for t in [0, 1, 63, 64, 255, 256, 5119, 5120, 15359, 15360, 15615, 15616, 15651, 15652]:
+        for h in (0, 6, 7, 13):
+            rows.add((0, t, h))
+    for _ in range(60):
+        rows.add((0, int(rng.integers(Sq)), int(rng.integers(Hq))))
+    rows = sorted(rows)
+    O_ref, L_ref = oracle.attention_rows(x.q, x.k, x.v, rows, None, True)
+    og = np.stack([o[b, t, h] for b, t, h in rows])
+    lg = np.array([lse[b, h, t] for b, t, h in rows])
+    err, _ = G.assert_parity(og, lg, O_ref, L_ref, "rounds sampled")
+    print(f"[fwd parity] rounds sampled {len(rows)} rows: max|dO| = {err:.3e}", flush=True)
+    assert not np.isnan(o).any() and not np.isnan(lse).any()
 
 
 def test_fwd_deterministic(aa):
