@@ -138,7 +138,7 @@ int fwd_impl(const void *q, const void *k, const void *v, void *o, float *lse, i
   if (batch <= 0 || seqlen_q <= 0 || seqlen_k <= 0 || n_q_heads <= 0 || n_kv_heads <= 0)
     return ATTN_ERR_INVALID;
   if (n_q_heads % n_kv_heads != 0) return ATTN_ERR_INVALID;
-  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128 && d != 256) return ATTN_ERR_UNSUPPORTED;
   const long wgs = (long)((seqlen_q + 255) / 256) * batch * n_q_heads;  // 256-row query tiles
   if (wgs > 0x7fffffffL) return ATTN_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (lse && !aligned4(lse)))
@@ -156,7 +156,7 @@ int fwd_varlen_impl(const void *q, const void *k, const void *v, const int32_t *
   if (batch <= 0 || max_seqlen_q <= 0 || total_q <= 0 || total_k < 0 || n_q_heads <= 0 || n_kv_heads <= 0)
     return ATTN_ERR_INVALID;
   if (n_q_heads % n_kv_heads != 0) return ATTN_ERR_INVALID;
-  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128 && d != 256) return ATTN_ERR_UNSUPPORTED;
   const long wgs = (long)((max_seqlen_q + 255) / 256) * batch * n_q_heads;
   if (wgs > 0x7fffffffL || (long long)total_q * n_q_heads > 0x7fffffffLL) return ATTN_ERR_UNSUPPORTED;
   if (!aligned16(q) || (k && !aligned16(k)) || (v && !aligned16(v)) || !aligned16(o) || (lse && !aligned4(lse)) ||

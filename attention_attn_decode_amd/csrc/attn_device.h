@@ -139,7 +139,9 @@ __device__ __forceinline__ uint2 lds_tr4_at(unsigned a) {
 // lanes of a transposing read of V - hit 16 distinct bank groups.
 template <int D>
 __device__ __forceinline__ int chunk_swz(int r) {
-  if constexpr (D == 128) return (4 * (r & 3)) | ((r >> 2) & 3);
+  // D = 256 (32 chunks, 512-byte rows) takes the D = 128 swizzle: it moves the
+  // low four chunk bits, which select the bank group.
+  if constexpr (D >= 128) return (4 * (r & 3)) | ((r >> 2) & 3);
   else return (4 * ((r >> 1) & 1)) | ((r >> 2) & 3);
 }
 

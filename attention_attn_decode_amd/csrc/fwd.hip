@@ -63,6 +63,10 @@ template <int D> struct VRow { static constexpr int v = D == 128 ? 160 : 96; };
 // stages V, each during its MFMA phase, ahead of use (one block through
 // registers at d = 64, two half-steps by direct-to-LDS loads at d = 128).
 constexpr int kBMP = 256;  // query rows per work-group
+// Keys per block: 64, or 32 at d = 256, where a block's score and probability
+// registers must shrink to leave room for the 32-row Q operands and O^T; a
+// phase still issues 32 MFMAs.
+template <int D> constexpr int kBlockKeys = D == 256 ? 32 : 64;
 
 // One 256-row query tile x (heaviest first: x / BH counts down the query
 // tiles, x % BH walks (sequence, head)) in the work-group's LDS block smem.
@@ -73,12 +77,12 @@ fwd_tile(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
          const int *__restrict__ cu_q, const int *__restrict__ cu_k, int total_q, int total_k,
          int Sq, int Sk, int Hq, int Hkv, int causal, float scale_log2, int n_mblocks, int BH, int x,
          uint16_t *smem) {
-  constexpr int BN = 64;
+  constexpr int BN = kBlockKeys<D>;
   constexpr int CH = D / 8;        // 16-byte chunks per row
-  // d = 128: K/V staged by direct-to-LDS buffer loads into three slots of
-  // dense, chunk-swizzled rows; d = 64: through registers into two slots of
-  // padded rows.
-  constexpr bool kDma = D == 128;
+  // d = 128 and 256: K/V staged by direct-to-LDS buffer loads into three
+  // slots of dense, chunk-swizzled rows; d = 64: through registers into two
+  // slots of padded rows.
+  constexpr bool kDma = D >= 128;
   constexpr int NSLOT = kDma ? 3 : 2;
   constexpr int KROW = kDma ? D : KRow<D>::v, VROW = kDma ? D : VRow<D>::v;
   constexpr int KT = BN * KROW, VT = BN * VROW;
@@ -176,26 +180,28 @@ fwd_tile(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
 #pragma unroll
     for (int qi = 0; qi < NKL; ++qi) sts16(dst + RPT * qi * drow, sreg[qi]);
   };
-  // Direct-to-LDS staging (d = 128): each wave of a group moves 16 rows of
-  // the block with four buffer loads whose 64 lanes deposit 16 bytes each,
-  // in lane order, at the LDS address in M0 (four dense 256-byte rows per
-  // load). Lane l of load i therefore fetches the chunk that the swizzle
-  // places at chunk l % 16 of row 4i + l / 16. All offsets are per lane, so
+  // Direct-to-LDS staging (d >= 128): each wave of a group moves BN / 4 rows
+  // of the block with buffer loads whose 64 lanes deposit 16 bytes each, in
+  // lane order, at the LDS address in M0 (1 KB: four 256-byte rows at
+  // d = 128, two 512-byte rows at d = 256). Lane l of load i therefore
+  // fetches the chunk that the swizzle places at chunk l % CH of row
+  // RPI i + l / CH. All offsets are per lane, so
   // the descriptor's range check zeroes rows past Sk. The compiler does not
   // see these writes: the waits that publish a slot are explicit. A load
   // that takes its LDS address from M0 needs one wait state after M0 is set.
-  constexpr int RPI = 64 / CH;  // rows per load
-  constexpr int NI = 16 / RPI;  // loads per wave per block
+  constexpr int RPI = 64 / CH;         // rows per load
+  constexpr int RPW = BN / 4;          // rows per wave of its group
+  constexpr int NI = RPW / RPI;        // loads per wave per block
   const int w4 = w & 3;
   int dvoff[kDma ? NI : 1];
   if constexpr (kDma) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int rw = 16 * w4 + RPI * i + lane / CH;
+      const int rw = RPW * w4 + RPI * i + lane / CH;
       dvoff[i] = (int)((rw * rstride + 8 * ((lane % CH) ^ chunk_swz<D>(rw))) * 2);
     }
   }
-  const unsigned lds_wave = lds_offset(dtile) + (unsigned)(16 * w4 * D * 2);
+  const unsigned lds_wave = lds_offset(dtile) + (unsigned)(RPW * w4 * D * 2);
   auto dma_blk = [&](int blk) {
     const __amdgpu_buffer_rsrc_t rs = rsrc_blk(blk);
     const unsigned slotb = lds_wave + (unsigned)(slot_of(blk) * dsize * 2);
@@ -463,7 +469,8 @@ fwd_tile(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
 }
 
 
-template <int D> constexpr int kTileLds = D == 128 ? 3 * 2 * 64 * D : 2 * 64 * (KRow<D>::v + VRow<D>::v);  // elements
+template <int D> constexpr int kTileLds =
+    D >= 128 ? 3 * 2 * kBlockKeys<D> * D : 2 * 64 * (KRow<D>::v + VRow<D>::v);  // elements
 // Waves per SIMD: two (one work-group per CU) at d = 128, four at d = 64,
 // where the kernel fits in 128 registers and two work-groups share a CU.
 template <int D> constexpr int kPrefillWaves = D == 64 ? 4 : 2;
@@ -486,8 +493,8 @@ fwd_pp(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
 // the heavy and light ends of consecutive rounds pair up on each CU. The
 // assignment is static: no counter, nothing to clear between calls. The
 // launcher takes it for dense batches at d = 128; a packed batch's empty
-// tiles would unbalance a static assignment, and at d = 64 two dispatched
-// work-groups per CU are faster.
+// tiles would unbalance a static assignment, at d = 64 two dispatched
+// work-groups per CU are faster, and at d = 256 the loop state would spill.
 template <int D, bool F16>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fwd_persist(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
@@ -535,6 +542,9 @@ hipError_t launch_fwd(const void *q, const void *k, const void *v, void *o, floa
     const int nwg = ntiles < ncu ? ntiles : ncu;
     if (f16) run(fwd_persist<128, true>, nwg);
     else run(fwd_persist<128, false>, nwg);
+  } else if (d == 256) {  // the persistent form's loop state would spill at d = 256
+    if (f16) run(fwd_pp<256, true>, ntiles);
+    else run(fwd_pp<256, false>, ntiles);
   } else if (d == 128) {
     if (f16) run(fwd_pp<128, true>, ntiles);
     else run(fwd_pp<128, false>, ntiles);

@@ -168,11 +168,12 @@ int attn_decode_f16(const void *q, const void *k_cache, const void *v_cache,
  * [batch][seqlen_k][n_kv_heads][d], all bf16; o like q; lse
  * [batch][n_q_heads][seqlen_q] fp32 (may be NULL). causal != 0 applies the
  * bottom-right mask (query i sees keys j <= i + seqlen_k - seqlen_q).
- * Requires d == 128 or d == 64. Work-groups of eight waves own 256 query rows
- * and take them heaviest first (longest visible key range first): at d = 128
- * one persistent work-group per compute unit walks the tile list in rounds
- * (the CU count is read from the current device; ATTN_ERR_LAUNCH if it cannot
- * be), at d = 64 one work-group is launched per tile. The tile order does not
+ * Requires d == 64, 128 or 256 (else ATTN_ERR_UNSUPPORTED). Work-groups of
+ * eight waves own 256 query rows and take them heaviest first (longest visible
+ * key range first): at d = 128 one persistent work-group per compute unit
+ * walks the tile list in rounds (the CU count is read from the current device;
+ * ATTN_ERR_LAUNCH if it cannot be), at d = 64 and 256 one work-group is
+ * launched per tile. The tile order does not
  * change the result: each row's output is computed by one wave in a fixed
  * order.
  */
@@ -199,8 +200,8 @@ int attn_fwd_f16(const void *q, const void *k, const void *v, void *o, float *ls
  *          inconsistent values cannot address outside the buffers.
  *   max_seqlen_q  at least the longest query length: it sizes the grid, and
  *          query rows past it are not computed.
- * A sequence with no keys gets O = 0 and LSE = -inf. Requires d == 64 or
- * d == 128 and total_q >= 1. Same tile code as attn_fwd, always one
+ * A sequence with no keys gets O = 0 and LSE = -inf. Requires d == 64, 128
+ * or 256 and total_q >= 1. Same tile code as attn_fwd, always one
  * work-group per (256-row query tile, sequence, query head), longest tile
  * index first; a work-group past its sequence's last tile exits at once (a
  * static persistent assignment would not see the lengths, which live on the

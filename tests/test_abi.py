@@ -121,6 +121,9 @@ def test_null_pointers_are_rejected_before_any_device_work():
     odd = ctypes.c_void_p(0x1002)
     assert L.attn_decode(odd, fake, fake, fake, fake, None, 8, 1, 64, 1, 1, 16, None, 0, None) == aa.ATTN_ERR_MISALIGNED
     assert L.attn_fwd(fake, fake, odd, fake, None, 1, 1, 16, 16, 8, 8, 64, None) == aa.ATTN_ERR_MISALIGNED
+    # d = 256 passes the head-size check of the prefill (the alignment check comes next)
+    assert L.attn_fwd(fake, fake, odd, fake, None, 1, 1, 16, 16, 8, 8, 256, None) == aa.ATTN_ERR_MISALIGNED
+    assert L.attn_fwd(fake, fake, fake, fake, None, 1, 1, 16, 16, 8, 8, 192, None) == aa.ATTN_ERR_UNSUPPORTED
     # workspace too small for a multi-piece plan
     assert L.attn_decode_ex(fake, fake, fake, fake, fake, None, 8, 1, 64, 1, 1, 4096, fake, 16, None, 4) == aa.ATTN_ERR_WORKSPACE
     assert L.attn_decode_ex(fake, fake, fake, fake, fake, None, 8, 1, 64, 1, 1, 4096, fake, 16, None, -1) == aa.ATTN_ERR_INVALID
@@ -148,6 +151,7 @@ def test_backward_validation_before_any_device_work():
     assert call(B=0) == aa.ATTN_ERR_INVALID and call(Sk=-1) == aa.ATTN_ERR_INVALID
     assert call(Hkv=3) == aa.ATTN_ERR_INVALID           # Hq % Hkv != 0
     assert call(d=96) == aa.ATTN_ERR_UNSUPPORTED
+    assert call(d=256) == aa.ATTN_ERR_UNSUPPORTED        # the backward takes d = 64 and 128 only
     assert call(dk=odd) == aa.ATTN_ERR_MISALIGNED and call(lse=ctypes.c_void_p(0x1001)) == aa.ATTN_ERR_MISALIGNED
     assert call(wsb=ws_ok - 4) == aa.ATTN_ERR_WORKSPACE
     assert call(fn=L.attn_bwd_f16, d=80) == aa.ATTN_ERR_UNSUPPORTED
@@ -167,6 +171,7 @@ def test_varlen_validation_before_any_device_work():
     assert call(B=0) == aa.ATTN_ERR_INVALID and call(mq=0) == aa.ATTN_ERR_INVALID and call(tq=0) == aa.ATTN_ERR_INVALID
     assert call(Hkv=3) == aa.ATTN_ERR_INVALID and call(d=32) == aa.ATTN_ERR_UNSUPPORTED
     assert call(cq=ctypes.c_void_p(0x1001)) == aa.ATTN_ERR_MISALIGNED and call(o=odd) == aa.ATTN_ERR_MISALIGNED
+    assert call(d=256, o=odd) == aa.ATTN_ERR_MISALIGNED   # d = 256 passes the head-size check
     assert call(fn=L.attn_fwd_varlen_f16, d=96) == aa.ATTN_ERR_UNSUPPORTED
 
 

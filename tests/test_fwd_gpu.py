@@ -48,6 +48,10 @@ def run_fwd(aa, x, causal=True):
     (1, 70, 1, 2, 1, 128, True),        # a single key: only the last row sees it
     (1, 1, 700, 2, 2, 128, True),       # one query row over a ragged key range
     (2, 333, 191, 4, 2, 128, False),    # ragged both ways, GQA, non-causal
+    (1, 300, 300, 2, 2, 256, True),     # head size 256: 32-key blocks
+    (2, 200, 333, 4, 1, 256, True),     # d = 256, GQA, bottom-right, ragged
+    (1, 333, 120, 2, 2, 256, False),    # d = 256, Sq > Sk, non-causal
+    (1, 1, 33, 1, 1, 256, True),
 ])
 def test_fwd_small_shapes(aa, shape):
     B, Sq, Sk, Hq, Hkv, d, causal = shape
@@ -142,6 +146,7 @@ def test_fwd_gqa_equals_mha_with_repeated_kv_heads(aa):
     (1, 300, 128, 2, 2, 128, True),
     (1, 257, 257, 2, 2, 128, False),
     (2, 64, 1000, 4, 4, 64, False),
+    (1, 300, 300, 2, 1, 256, True),
 ])
 def test_fwd_f16_small_shapes(aa, shape):
     """IEEE fp16 inputs and outputs (attn_fwd_f16) against the oracle reading the same fp16 bits."""

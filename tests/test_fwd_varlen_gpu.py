@@ -40,6 +40,7 @@ CASES = [
     ([77, 300, 5, 256], [77, 300, 5, 256], 4, 4, 64, False),
     ([129, 0, 40], [129, 50, 0], 3, 1, 128, True),                         # an empty query range, an empty key range
     ([1000], [1000], 2, 1, 64, True),
+    ([150, 0, 300, 33], [150, 40, 300, 90], 4, 2, 256, True),            # d = 256, an empty query range
 ]
 
 
