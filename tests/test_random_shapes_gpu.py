@@ -64,11 +64,11 @@ def test_random_decode(aa, case):
     G.assert_parity(G.host_f64(o), G.host_f64(lse), O_ref, L_ref, f"decode case {case}")
 
 
-def _prefill_cases(n, seed=921):
+def _prefill_cases(n, seed=921, dims=(64, 128)):
     rng = np.random.default_rng(seed)
     out = []
     for i in range(n):
-        d = int(rng.choice([64, 128]))
+        d = int(rng.choice(dims))
         Hkv = int(rng.choice([1, 2, 4]))
         Hq = Hkv * int(rng.choice([1, 2, 4]))
         B = int(rng.integers(1, 3))
@@ -80,7 +80,8 @@ def _prefill_cases(n, seed=921):
     return out
 
 
-@pytest.mark.parametrize("case", _prefill_cases(12), ids=lambda c: f"fwd{c[0]}")
+@pytest.mark.parametrize("case", _prefill_cases(12) + [(12 + c[0],) + c[1:] for c in _prefill_cases(6, seed=927, dims=(256,))],
+                         ids=lambda c: f"fwd{c[0]}")
 def test_random_prefill(aa, case):
     i, B, Sq, Sk, Hq, Hkv, d, causal, dtype = case
     torch = G.torch()
