@@ -181,7 +181,7 @@ def main():
         ingest_counters(*args.ingest_counters)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
 
@@ -205,7 +205,7 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
     # ---- decode workload (cache at capacity, rows past each sequence end zero) ----
-    dc = wl.DECODE_CONFIGS["c2"]
+    dc = wl.DECODE_CONFIGS["gqa-decode"]
     t0 = time.perf_counter()
     xd = wl.decode_inputs(dc, pad=wl.BF16_ZERO)
     B, sq, Hq, d = xd.q.shape
@@ -226,7 +226,7 @@ def main():
     # ---- prefill workload ----
     run_prefill = not args.no_prefill
     if run_prefill:
-        pc = wl.PREFILL_CONFIGS["c5"]
+        pc = wl.PREFILL_CONFIGS["causal-prefill"]
         xp = wl.prefill_inputs(pc)
         qp, kp, vp = to_dev(xp.q), to_dev(xp.k), to_dev(xp.v)
         op = torch.empty_like(qp)

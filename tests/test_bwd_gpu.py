@@ -136,20 +136,20 @@ def test_bwd_gqa_equals_mha_with_summed_heads(aa):
 def test_bwd_causal_prefill_workload_sampled(aa):
     """Full-size causal prefill backward (B=2, 32 heads, S=8192, d=128): one head against the
     oracle element by element, and a property of every head (sum_j dV_j = sum_i dO_i)."""
-    x = wl.prefill_inputs("c5")
+    x = wl.prefill_inputs("causal-prefill")
     do = wl.make_grad_out(x.q, 1005)
     B, S, H, d = x.q.shape
-    print(f"[bwd parity] c5 shape {x.q.shape}", flush=True)
+    print(f"[bwd parity] causal prefill shape {x.q.shape}", flush=True)
     dq, dk, dv = run_bwd(aa, x, do)
     b, h = 1, 5
     rq, rk, rv, _ = oracle.backward_kv_head(x.q, x.k, x.v, do, b, h, True)
     sl = (slice(b, b + 1), slice(None), slice(h, h + 1))
     eq, ek, ev = oracle.backward_error_scales(x.q[sl], x.k[sl], x.v[sl], do[sl], True)
     u = U["bf16"]
-    w = (assert_grad_parity(dq[b, :, h], rq[:, 0], eq[0, :, 0], u, "c5 dq"),
-         assert_grad_parity(dk[b, :, h], rk, ek[0, :, 0], u, "c5 dk"),
-         assert_grad_parity(dv[b, :, h], rv, ev[0, :, 0], u, "c5 dv"))
-    print(f"[bwd parity] c5 head (1, 5): err/bound dq {w[0]:.3f} dk {w[1]:.3f} dv {w[2]:.3f}", flush=True)
+    w = (assert_grad_parity(dq[b, :, h], rq[:, 0], eq[0, :, 0], u, "causal prefill dq"),
+         assert_grad_parity(dk[b, :, h], rk, ek[0, :, 0], u, "causal prefill dk"),
+         assert_grad_parity(dv[b, :, h], rv, ev[0, :, 0], u, "causal prefill dv"))
+    print(f"[bwd parity] causal prefill head (1, 5): err/bound dq {w[0]:.3f} dk {w[1]:.3f} dv {w[2]:.3f}", flush=True)
     # Every row sees a key (causal, Sq == Sk), so the dV rows of a head sum to its dO rows:
     # sum_j dV_j = sum_i dO_i exactly, and to u (sum_i |dO_i| + sum_j |dV_j|) after roundings.
     dof = oracle.bf16_bits_to_f64(do)

@@ -74,9 +74,9 @@ def test_fwd_page_correctness_config(aa):
 
 def test_fwd_causal_prefill_workload_sampled(aa):
     """Full-size causal prefill (B=2, 32 heads, S=8192, d=128), oracle on sampled rows."""
-    x = wl.prefill_inputs("c5")
+    x = wl.prefill_inputs("causal-prefill")
     B, S, H, d = x.q.shape
-    print(f"[fwd parity] c5 shape {x.q.shape}", flush=True)
+    print(f"[fwd parity] causal prefill shape {x.q.shape}", flush=True)
     o, lse = run_fwd(aa, x, True)
     rng = np.random.default_rng(5)
     rows = set()
@@ -88,8 +88,8 @@ def test_fwd_causal_prefill_workload_sampled(aa):
     O_ref, L_ref = oracle.attention_rows(x.q, x.k, x.v, rows, None, True)
     og = np.stack([o[b, t, h] for b, t, h in rows])
     lg = np.array([lse[b, h, t] for b, t, h in rows])
-    err, scale = G.assert_parity(og, lg, O_ref, L_ref, "c5 sampled")
-    print(f"[fwd parity] c5 sampled {len(rows)} rows: max|dO| = {err:.3e}", flush=True)
+    err, scale = G.assert_parity(og, lg, O_ref, L_ref, "causal prefill sampled")
+    print(f"[fwd parity] causal prefill sampled {len(rows)} rows: max|dO| = {err:.3e}", flush=True)
     # property at any size: O rows are convex combinations of V rows -> |O| <= max|V| per column
     assert np.abs(o).max() <= np.abs(oracle.bf16_bits_to_f64(x.v)).max() + 1e-2
 

@@ -112,17 +112,17 @@ class PrefillConfig:
 
 # The five workloads, with seeds 1000 + index (index 0..4).
 DECODE_CONFIGS = {
-    "c1": DecodeConfig("c1", 1, 8, 1, 64, 1, 512, 512, 512, 1000,
+    "gqa-decode-small": DecodeConfig("gqa-decode-small", 1, 8, 1, 64, 1, 512, 512, 512, 1000,
                        "single-token GQA decode, 8 q heads on 1 kv head, d=64, L=512"),
-    "c2": DecodeConfig("c2", 32, 64, 8, 128, 1, 8192, 1024, 8192, 1001,
+    "gqa-decode": DecodeConfig("gqa-decode", 32, 64, 8, 128, 1, 8192, 1024, 8192, 1001,
                        "GQA decode, B=32, 64/8 heads, d=128, L ~ U{1024..8192}"),
-    "c3": DecodeConfig("c3", 16, 32, 8, 64, 4, 4096, 4096, 4096, 1002,
+    "multi-token-decode": DecodeConfig("multi-token-decode", 16, 32, 8, 64, 4, 4096, 4096, 4096, 1002,
                        "multi-token decode, B=16, 32/8 heads, d=64, 4 causal new tokens, L=4096"),
-    "c4": DecodeConfig("c4", 4, 32, 8, 128, 1, 131072, 131072, 131072, 1003,
+    "long-context-decode": DecodeConfig("long-context-decode", 4, 32, 8, 128, 1, 131072, 131072, 131072, 1003,
                        "long-context decode, B=4, 32/8 heads, d=128, L=131072"),
 }
 PREFILL_CONFIGS = {
-    "c5": PrefillConfig("c5", 2, 32, 32, 128, 8192, True, 1004,
+    "causal-prefill": PrefillConfig("causal-prefill", 2, 32, 32, 128, 8192, True, 1004,
                         "causal prefill, B=2, 32 heads MHA, d=128, S=8192"),
 }
 
