@@ -123,6 +123,23 @@ __device__ __forceinline__ uint2 lds_tr4(const uint16_t *p) {
   return __builtin_bit_cast(uint2, v);
 }
 
+// Direct-to-LDS buffer load: each of the wave's 64 lanes fetches 16 bytes at
+// voffset through the descriptor (out-of-range offsets read zero) and the
+// wave deposits them in lane order, 1 KB, at LDS byte address lds (wave
+// uniform). The compiler does not see the LDS write: the caller waits
+// (vmcnt) before the barrier that publishes the data. A load that takes its
+// LDS address from M0 needs one wait state after M0 is set. M0 is listed as
+// clobbered; the compiler warns because it reserves M0, and the kernels that
+// use this leave M0 to these loads alone.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, int voffset, unsigned lds) {
+  const unsigned la = __builtin_amdgcn_readfirstlane(lds);
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voffset), "s"(rs), "s"(la)
+               : "memory", "m0");
+#pragma clang diagnostic pop
+}
+
 // lds_tr4 at an LDS byte address.
 __device__ __forceinline__ uint2 lds_tr4_at(unsigned a) {
   typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;

@@ -67,6 +67,12 @@ template <int D> constexpr bool kLateLoads = D == 64;
 // kernels past their budget and the spills cost more than the ring saves.
 template <int D> constexpr bool kOperandRing = D == 64;
 
+// dQ at d = 128 stages its K and V tiles with direct-to-LDS loads (waves 0-3
+// K, waves 4-7 V, 16 rows each), which frees the 16 staging registers per
+// thread the operand ring needs there.
+template <int D> constexpr bool kDqDma = D == 128;
+template <int D> constexpr bool kDqRing = kOperandRing<D> || kDqDma<D>;
+
 __device__ __forceinline__ int pi_row(int i) { return (i & ~12) | ((i >> 1) & 4) | ((i << 1) & 8); }
 
 // Row-major tile of R rows x D elements in LDS, 16-byte chunks XOR-swizzled
@@ -463,7 +469,26 @@ bwd_dq(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uin
 
   const size_t rstride = (size_t)Hkv * D;
   const int trow = tid / CH, tch = tid % CH;
-  uint4 sk[LPT], sv[LPT];
+  // Direct loads (d = 128): load i of wave w (group w / 4: K or V) fills rows
+  // 16 (w % 4) + 4 i .. +3 of the tile, lane l fetching the chunk that the
+  // swizzle places at chunk l % 16 of row 4 i + l / 16.
+  int dvoff[kDqDma<D> ? 4 : 1];
+  if constexpr (kDqDma<D>) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * (w & 3) + 4 * i + lane / CH;
+      dvoff[i] = (int)((r * rstride + 8 * ((lane % CH) ^ chunk_swz<D>(r))) * 2);
+    }
+  }
+  auto dma_blk = [&](int blk) {
+    const long long base = ((long long)kbase * Hkv + gk) * D + (long long)blk * kKB * rstride;
+    const long long left = ((long long)Sk * Hkv - gk) * D * 2 - (long long)blk * kKB * rstride * 2;
+    const auto rs = buffer_rsrc((w < 4 ? k : v) + base, left);
+    const unsigned tile = lds_offset(smem + (blk & 1) * 2 * KTL + (w < 4 ? 0 : KTL)) + 16 * (w & 3) * D * 2;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lds_dma16(rs, dvoff[i], tile + 4 * i * D * 2);
+  };
+  uint4 sk[kDqDma<D> ? 1 : LPT], sv[kDqDma<D> ? 1 : LPT];
   auto load_blk = [&](int blk) {
     const long long base = ((long long)kbase * Hkv + gk) * D + (long long)blk * kKB * rstride;
     const long long left = ((long long)Sk * Hkv - gk) * D * 2 - (long long)blk * kKB * rstride * 2;
@@ -485,13 +510,18 @@ bwd_dq(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uin
     }
   };
 
-  if (nblk > 0) {
+  if constexpr (kDqDma<D>) {
+    if (nblk > 0) dma_blk(0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), seen by the compiler: none of its loads is pending in the loop
+  } else if (nblk > 0) {
     load_blk(0);
     store_blk(0);
   }
   __syncthreads();
   for (int j = 0; j < nblk; ++j) {
-    if constexpr (!kLateLoads<D>) {
+    if constexpr (kDqDma<D>) {
+      if (j + 1 < nblk) dma_blk(j + 1);  // into the slot block j - 1 held, read before the last barrier
+    } else if constexpr (!kLateLoads<D>) {
       if (j + 1 < nblk) load_blk(j + 1);
     }
     const int j0 = j * kKB;
@@ -501,7 +531,7 @@ bwd_dq(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uin
       __builtin_amdgcn_s_setprio(2);
       // S = K Q^T and dP = V dO^T for the two 32-key halves.
       f32x16 S[2], dP[2];
-      if constexpr (kOperandRing<D>) {
+      if constexpr (kDqRing<D>) {
         mfma_stream<4 * KST, 3>(
             [&](auto gc) {
               constexpr int g = decltype(gc)::value, t = g / (2 * KST), kk = (g / 2) % KST;
@@ -557,7 +587,7 @@ bwd_dq(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uin
         if (j + 1 < nblk) load_blk(j + 1);
       }
       __builtin_amdgcn_s_setprio(2);
-      if constexpr (kOperandRing<D>) {
+      if constexpr (kDqRing<D>) {
         mfma_stream<4 * MT, 3>(
             [&](auto gc) {
               constexpr int g = decltype(gc)::value;
@@ -578,7 +608,11 @@ bwd_dq(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uin
     if constexpr (kLateLoads<D>) {
       if (!active && j + 1 < nblk) load_blk(j + 1);
     }
-    if (j + 1 < nblk) store_blk((j + 1) & 1);
+    if constexpr (kDqDma<D>) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // block j + 1 is in LDS before the barrier
+    } else {
+      if (j + 1 < nblk) store_blk((j + 1) & 1);
+    }
     __syncthreads();
   }
 

@@ -187,8 +187,7 @@ fwd_tile(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
   // fetches the chunk that the swizzle places at chunk l % CH of row
   // RPI i + l / CH. All offsets are per lane, so
   // the descriptor's range check zeroes rows past Sk. The compiler does not
-  // see these writes: the waits that publish a slot are explicit. A load
-  // that takes its LDS address from M0 needs one wait state after M0 is set.
+  // see these writes: the waits that publish a slot are explicit.
   constexpr int RPI = 64 / CH;         // rows per load
   constexpr int RPW = BN / 4;          // rows per wave of its group
   constexpr int NI = RPW / RPI;        // loads per wave per block
@@ -206,16 +205,7 @@ fwd_tile(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const __amdgpu_buffer_rsrc_t rs = rsrc_blk(blk);
     const unsigned slotb = lds_wave + (unsigned)(slot_of(blk) * dsize * 2);
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const unsigned la = __builtin_amdgcn_readfirstlane(slotb + RPI * i * D * 2);
-      // M0 is listed as clobbered; the compiler warns because it reserves
-      // M0, and this kernel leaves M0 to these loads alone.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-      asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(dvoff[i]), "s"(rs), "s"(la)
-                   : "memory", "m0");
-#pragma clang diagnostic pop
-    }
+    for (int i = 0; i < NI; ++i) lds_dma16(rs, dvoff[i], slotb + RPI * i * D * 2);
   };
   // Wait until at most one block's direct loads (the newest) are in flight.
   auto dma_wait_one = [&]() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NI) : "memory"); };
