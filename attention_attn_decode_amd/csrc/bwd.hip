@@ -72,6 +72,11 @@ template <int D> constexpr bool kOperandRing = D == 64;
 // thread the operand ring needs there.
 template <int D> constexpr bool kDqDma = D == 128;
 template <int D> constexpr bool kDqRing = kOperandRing<D> || kDqDma<D>;
+// dK/dV at d = 128 likewise: Q and dO tiles by direct loads (waves 0-3 Q,
+// 4-7 dO, 8 rows each), and the operand ring on the dV/dK products, whose
+// operands all come from LDS.
+template <int D> constexpr bool kDkdvDma = D == 128;
+template <int D> constexpr bool kDkdvRing2 = kOperandRing<D> || kDkdvDma<D>;
 
 __device__ __forceinline__ int pi_row(int i) { return (i & ~12) | ((i >> 1) & 4) | ((i << 1) & 8); }
 
@@ -234,8 +239,30 @@ bwd_dkdv(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const u
 
   const size_t rstride = (size_t)Hq * D;
   const int tg = tid, trow = tg / CH, tch = tg % CH;
-  uint4 sq[LPT], sdo[LPT];
+  uint4 sq[kDkdvDma<D> ? 1 : LPT], sdo[kDkdvDma<D> ? 1 : LPT];
   float sst;  // threads 0-63: the L2 (0-31) or D (32-63) value of one of the step's rows
+  // Direct loads (d = 128): load i of wave w fills rows 8 (w % 4) + 4 i .. +3
+  // of the Q (w < 4) or dO tile; lane l fetches the chunk that the swizzle
+  // places at chunk l % 16 of its row.
+  int dvoff[kDkdvDma<D> ? 2 : 1];
+  if constexpr (kDkdvDma<D>) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = 8 * (w & 3) + 4 * i + lane / CH;
+      dvoff[i] = (int)((r * rstride + 8 * ((lane % CH) ^ chunk_swz<D>(r))) * 2);
+    }
+  }
+  auto dma_step = [&](int st) {
+    const int hh = st / (nqb - ib0), ib = ib0 + st % (nqb - ib0);
+    const int h = g * G + hh;
+    if (tid < 64) sst = (tid < 32 ? l2ws : dws)[stat_b + (size_t)h * Sq_pad + ib * kQB + (tid & 31)];
+    const long long base = ((long long)qbase * Hq + h) * D + (long long)ib * kQB * rstride;
+    const long long left = ((long long)Sq * Hq - h) * D * 2 - (long long)ib * kQB * rstride * 2;
+    const auto rs = uniform_buffer_rsrc((w < 4 ? q : dout) + base, left);
+    const unsigned tile = lds_offset(smem + (st & 1) * 2 * QT + (w < 4 ? 0 : QT)) + 8 * (w & 3) * D * 2;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) lds_dma16(rs, dvoff[i], tile + 4 * i * D * 2);
+  };
   auto load_step = [&](int st) {
     const int hh = st / (nqb - ib0), ib = ib0 + st % (nqb - ib0);
     const int h = g * G + hh;
@@ -261,13 +288,19 @@ bwd_dkdv(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const u
     if (tid < 64) stat[slot][tid >> 5][tid & 31] = sst;
   };
 
-  if (nsteps > 0) {
+  if constexpr (kDkdvDma<D>) {
+    if (nsteps > 0) dma_step(0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), seen by the compiler: none of its loads is pending in the loop
+    if (nsteps > 0 && tid < 64) stat[0][tid >> 5][tid & 31] = sst;
+  } else if (nsteps > 0) {
     load_step(0);
     store_step(0);
   }
   __syncthreads();
   for (int st = 0; st < nsteps; ++st) {
-    if constexpr (!kLateLoads<D>) {
+    if constexpr (kDkdvDma<D>) {
+      if (st + 1 < nsteps) dma_step(st + 1);  // into the slot step st - 1 held, read before the last barrier
+    } else if constexpr (!kLateLoads<D>) {
       if (st + 1 < nsteps) load_step(st + 1);
     }
     const int ib = ib0 + st % (nqb - ib0);
@@ -349,7 +382,7 @@ bwd_dkdv(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const u
         if (st + 1 < nsteps) load_step(st + 1);
       }
       __builtin_amdgcn_s_setprio(2);
-      if constexpr (kOperandRing<D>) {
+      if constexpr (kDkdvRing2<D>) {
         // dV^T += dO^T P^T and dK^T += Q^T dS^T as one stream.
         mfma_stream<4 * MT, 3>(
             [&](auto gc) {
@@ -375,7 +408,14 @@ bwd_dkdv(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const u
     if constexpr (kLateLoads<D>) {
       if (!active && st + 1 < nsteps) load_step(st + 1);
     }
-    if (st + 1 < nsteps) store_step((st + 1) & 1);
+    if constexpr (kDkdvDma<D>) {
+      if (st + 1 < nsteps) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // step st + 1's tiles are in LDS before the barrier
+        if (tid < 64) stat[(st + 1) & 1][tid >> 5][tid & 31] = sst;
+      }
+    } else {
+      if (st + 1 < nsteps) store_step((st + 1) & 1);
+    }
     __syncthreads();
   }
 
