@@ -63,8 +63,8 @@ constexpr float kLog2e = 1.44269504088896340736f;
 template <int D> constexpr bool kLateLoads = D == 64;
 
 // LDS operands read three MFMAs ahead of their product through a register
-// ring (mfma_stream) at d = 64. At d = 128 the ring's registers push both
-// kernels past their budget and the spills cost more than the ring saves.
+// ring (mfma_stream) at d = 64. At d = 128 the ring fits only where direct
+// loads free the staging registers (kDqRing, kDkdvRing2 below).
 template <int D> constexpr bool kOperandRing = D == 64;
 
 // dQ at d = 128 stages its K and V tiles with direct-to-LDS loads (waves 0-3
