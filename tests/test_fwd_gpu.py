@@ -166,3 +166,50 @@ def test_fwd_page_correctness_config_in_its_dtype(aa):
     o, lse = run_fwd(aa, x, True)
     assert np.allclose(o, O_ref, rtol=g["rtol"], atol=g["atol"])
     G.assert_parity(o, lse, O_ref, L_ref, "fa4 correctness config, fp16")
+
+
+def test_prefill_graph_replay_without_memset(aa):
+    """Captured prefill calls (the persistent d = 128 grid, whose launch reads
+    the CU count, and the packed d = 64 path), replayed with new queries; each
+    replay must equal an eager call on the same inputs and match the oracle."""
+    torch = G.torch()
+    B, S, Hq, Hkv, d = 1, 700, 4, 2, 128
+    x = wl.make_prefill(B, Hq, Hkv, d, S, S, seed=151)
+    q, k, v = G.dev_bf16(x.q), G.dev_bf16(x.k), G.dev_bf16(x.v)
+    o = G.nan_like_bf16((B, S, Hq, d))
+    lse = G.nan_f32((B, Hq, S))
+    xv = wl.make_varlen([300, 0, 257], [300, 40, 400], 2, 1, 64, seed=153)
+    qv, kv, vv = G.dev_bf16(xv.q), G.dev_bf16(xv.k), G.dev_bf16(xv.v)
+    cq, ck = G.dev_i32(xv.cu_q), G.dev_i32(xv.cu_k)
+    ov = G.nan_like_bf16(qv.shape)
+    lv = G.nan_f32((qv.shape[1], qv.shape[0]))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+
+    def calls(stream):
+        aa.attn_fwd(q, k, v, o, lse, causal=True, stream=stream)
+        aa.attn_fwd_varlen(qv, kv, vv, cq, ck, ov, 300, lse=lv, causal=True, stream=stream)
+
+    with torch.cuda.stream(s):
+        calls(s)  # warm-up outside capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        calls(s)
+    for rep in range(3):
+        xq = wl.make_prefill(B, Hq, Hkv, d, S, S, seed=160 + rep)
+        q.copy_(G.dev_bf16(xq.q))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        og, lg, ovg, lvg = G.host_f64(o), G.host_f64(lse), G.host_f64(ov), G.host_f64(lv)
+        o2, l2 = G.nan_like_bf16((B, S, Hq, d)), G.nan_f32((B, Hq, S))
+        aa.attn_fwd(q, k, v, o2, l2, causal=True)
+        ov2, lv2 = G.nan_like_bf16(qv.shape), G.nan_f32((qv.shape[1], qv.shape[0]))
+        aa.attn_fwd_varlen(qv, kv, vv, cq, ck, ov2, 300, lse=lv2, causal=True)
+        torch.cuda.synchronize()
+        assert np.array_equal(og, G.host_f64(o2)) and np.array_equal(lg, G.host_f64(l2)), f"dense replay {rep}"
+        assert np.array_equal(ovg, G.host_f64(ov2)) and np.array_equal(lvg, G.host_f64(lv2)), f"packed replay {rep}"
+        O_ref, L_ref = oracle.attention(xq.q, x.k, x.v, None, True)
+        G.assert_parity(og, lg, O_ref, L_ref, f"prefill graph replay {rep}")
