@@ -334,7 +334,9 @@ const char *attn_status_string(int status) {
   switch (status) {
     case ATTN_OK: return "ok";
     case ATTN_ERR_INVALID: return "invalid argument";
-    case ATTN_ERR_UNSUPPORTED: return "unsupported shape (d must be 64 or 128; packed query rows <= 32)";
+    case ATTN_ERR_UNSUPPORTED:
+      return "unsupported shape (decode and forward: d in {64, 128, 256}; backward: d in {64, 128}; "
+             "decode: packed query rows per KV head <= 32, <= 16 at d = 256, batch <= 8192)";
     case ATTN_ERR_MISALIGNED: return "pointer not 16-byte aligned";
     case ATTN_ERR_WORKSPACE: return "workspace too small";
     case ATTN_ERR_LAUNCH: return "HIP kernel launch failed";

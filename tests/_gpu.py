@@ -65,3 +65,25 @@ def assert_parity(o, lse, O_ref, LSE_ref, tag=""):
             rel = np.abs(lse[fin] - LSE_ref[fin]) / np.maximum(1.0, np.abs(LSE_ref[fin]))
             assert rel.max() <= LSE_RTOL, f"{tag}: LSE rel err {rel.max():.3e}"
     return err, scale
+
+
+def host_threads() -> int:
+    """Worker threads for oracle checks: the host cores this process may use (at most 16)."""
+    import os
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def parallel_map(fn, items):
+    """fn over items on host_threads() threads, BLAS held to one thread each (NumPy
+    releases the interpreter lock inside BLAS calls and large array loops, so the
+    oracle's per-head work runs in parallel). Returns the results in item order;
+    the first exception raised by any call is re-raised."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1), ThreadPoolExecutor(host_threads()) as ex:
+        return list(ex.map(fn, items))

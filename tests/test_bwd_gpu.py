@@ -158,6 +158,30 @@ def test_bwd_causal_prefill_workload_sampled(aa):
     assert np.all(np.abs(lhs - rhs) <= tol)
 
 
+@pytest.mark.parametrize("b", [0, 1])
+def test_bwd_causal_prefill_workload_every_head(aa, b):
+    """Full-size causal prefill backward (B=2, 32 heads, S=8192, d=128): dQ, dK and dV of
+    every head of batch row b against the oracle element by element, within the
+    rounding bound, heads in parallel (the two rows together cover all 64 pairs)."""
+    x = wl.prefill_inputs("causal-prefill")
+    do = wl.make_grad_out(x.q, 1005)
+    B, S, H, d = x.q.shape
+    print(f"[bwd parity] causal prefill every head, shape {x.q.shape}", flush=True)
+    dq, dk, dv = run_bwd(aa, x, do)
+    u = U["bf16"]
+
+    def head(h):
+        rq, rk, rv, _ = oracle.backward_kv_head(x.q, x.k, x.v, do, b, h, True)
+        sl = (slice(b, b + 1), slice(None), slice(h, h + 1))
+        eq, ek, ev = oracle.backward_error_scales(x.q[sl], x.k[sl], x.v[sl], do[sl], True)
+        return max(assert_grad_parity(dq[b, :, h], rq[:, 0], eq[0, :, 0], u, f"({b}, {h}) dq"),
+                   assert_grad_parity(dk[b, :, h], rk, ek[0, :, 0], u, f"({b}, {h}) dk"),
+                   assert_grad_parity(dv[b, :, h], rv, ev[0, :, 0], u, f"({b}, {h}) dv"))
+
+    worst = G.parallel_map(head, list(range(H)))
+    print(f"[bwd parity] causal prefill batch row {b}, every head: worst err/bound {max(worst):.3f}", flush=True)
+
+
 # --- packed variable-length batches -------------------------------------------
 
 def run_bwd_varlen(aa, x, do_bits, causal=True):

@@ -94,6 +94,43 @@ def test_fwd_causal_prefill_workload_sampled(aa):
     assert np.abs(o).max() <= np.abs(oracle.bf16_bits_to_f64(x.v)).max() + 1e-2
 
 
+def test_fwd_causal_prefill_workload_every_row(aa):
+    """Full-size causal prefill (B=2, 32 heads, S=8192, d=128): every one of the
+    524,288 (batch, query, head) rows of O and LSE against the oracle at the
+    parity bar, one (batch, head) per oracle call, heads in parallel."""
+    x = wl.prefill_inputs("causal-prefill")
+    B, S, H, d = x.q.shape
+    print(f"[fwd parity] causal prefill every row, shape {x.q.shape}", flush=True)
+    o, lse = run_fwd(aa, x, True)
+
+    def head(bh):
+        b, h = bh
+        sl = (slice(b, b + 1), slice(None), slice(h, h + 1))
+        O_ref, L_ref = oracle.attention(x.q[sl], x.k[sl], x.v[sl], None, True)
+        return G.assert_parity(o[sl], lse[b:b + 1, h:h + 1], O_ref, L_ref, f"causal prefill (b={b}, h={h})")[0]
+
+    errs = G.parallel_map(head, [(b, h) for b in range(B) for h in range(H)])
+    print(f"[fwd parity] causal prefill every row: {B * S * H} rows, max|dO| = {max(errs):.3e}", flush=True)
+
+
+def test_fwd_tile_rounds_ragged_gqa_every_row(aa):
+    """The 868-tile ragged GQA prefill of the sampled test below (Sq = 15653 < Sk = 15700,
+    14 query heads on 2 KV heads): every row against the oracle, heads in parallel."""
+    B, Sq, Sk, Hq, Hkv, d = 1, 15653, 15700, 14, 2, 128
+    x = wl.make_prefill(B, Hq, Hkv, d, Sq, Sk, seed=97)
+    print(f"[fwd parity] rounds every row, q {x.q.shape} k {x.k.shape}", flush=True)
+    o, lse = run_fwd(aa, x, True)
+    Gq = Hq // Hkv
+
+    def head(h):
+        g = h // Gq
+        O_ref, L_ref = oracle.attention(x.q[:, :, h:h + 1], x.k[:, :, g:g + 1], x.v[:, :, g:g + 1], None, True)
+        return G.assert_parity(o[:, :, h:h + 1], lse[:, h:h + 1], O_ref, L_ref, f"rounds head {h}")[0]
+
+    errs = G.parallel_map(head, list(range(Hq)))
+    print(f"[fwd parity] rounds every row: {Sq * Hq} rows, max|dO| = {max(errs):.3e}", flush=True)
+
+
 def test_fwd_tile_rounds_ragged_gqa_sampled(aa):
     """868 query tiles (62 of 256 rows x 14 heads): three full rounds of resident
     work-groups and a partial reversed fourth, ragged Sq = 15653 < Sk = 15700
