@@ -21,6 +21,8 @@ ATTN_ERR_MISALIGNED = -3
 ATTN_ERR_WORKSPACE = -4
 ATTN_ERR_LAUNCH = -5
 ATTN_ERR_DEVICE = -6
+ATTN_ERR_TOO_LARGE = -7
+ATTN_NOALLOC_SCRATCH_BYTES = 32 << 20
 ATTN_MAX_PIECES = 4096
 ATTN_MIN_PIECE = 64
 ATTN_MAX_BATCH = 8192
@@ -30,7 +32,7 @@ EXPORTS = ("attn_decode_plan", "attn_decode_workspace_size", "attn_decode", "att
            "attn_decode_f16", "attn_fwd", "attn_fwd_f16", "attn_fwd_varlen", "attn_fwd_varlen_f16",
            "attn_bwd_workspace_size", "attn_bwd", "attn_bwd_varlen_workspace_size", "attn_bwd_varlen",
            "attn_bwd_varlen_f16",
-           "attn_bwd_f16", "attn_status_string", "attn_version")
+           "attn_bwd_f16", "attn_decode_noalloc", "attn_status_string", "attn_version")
 
 _lib = None
 
@@ -61,6 +63,8 @@ def lib() -> ctypes.CDLL:
     for name in ("attn_decode_ex", "attn_decode_f16"):
         getattr(L, name).argtypes = dec + [i32]
         getattr(L, name).restype = i32
+    L.attn_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, i32]
+    L.attn_decode_noalloc.restype = i32
     for name in ("attn_fwd", "attn_fwd_f16"):
         getattr(L, name).argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp]
         getattr(L, name).restype = i32
@@ -183,6 +187,38 @@ def attn_decode(q, k_cache, v_cache, seqlens_k, o, lse=None, workspace=None, num
             _ptr(workspace), wbytes, _stream_ptr(stream), int(num_splits))
     if st != ATTN_OK:
         raise AttnError(st, "attn_decode")
+
+
+def _decode_shapes(q, k_cache, v_cache, seqlens_k, o, lse, et):
+    import torch
+    _check(q, "q", et, 4)
+    _check(k_cache, "k_cache", et, 4)
+    _check(v_cache, "v_cache", et, 4)
+    _check(seqlens_k, "seqlens_k", torch.int32, 1)
+    _check(o, "o", et, 4)
+    B, sq, Hq, d = q.shape
+    _, S, Hkv, dk = k_cache.shape
+    if tuple(v_cache.shape) != tuple(k_cache.shape) or dk != d or k_cache.shape[0] != B:
+        raise ValueError("k_cache/v_cache must be [B, S_max, Hkv, d] matching q")
+    if tuple(o.shape) != tuple(q.shape) or seqlens_k.shape[0] != B:
+        raise ValueError("o must match q and seqlens_k must have B entries")
+    if lse is not None:
+        _check(lse, "lse", torch.float32, 3)
+        if tuple(lse.shape) != (B, Hq, sq):
+            raise ValueError("lse must be [B, Hq, sq]")
+    return B, sq, Hq, d, S, Hkv
+
+
+def attn_decode_noalloc(q, k_cache, v_cache, seqlens_k, o, lse=None, num_splits=0, stream=None):
+    """attn_decode (bf16) without a workspace: the library's fixed per-device scratch
+    holds the partials (ATTN_NOALLOC_SCRATCH_BYTES); nothing is allocated. Calls that
+    overlap on one device race on that scratch."""
+    import torch
+    B, sq, Hq, d, S, Hkv = _decode_shapes(q, k_cache, v_cache, seqlens_k, o, lse, torch.bfloat16)
+    st = lib().attn_decode_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens_k), _ptr(o), _ptr(lse),
+                                   Hq, Hkv, d, sq, B, S, _stream_ptr(stream), int(num_splits))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_decode_noalloc")
 
 
 def attn_fwd(q, k, v, o, lse=None, causal=True, stream=None):

@@ -3,6 +3,7 @@
 // every entry point live in include/attn.h.
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include <hip/hip_runtime.h>
 
@@ -99,6 +100,32 @@ size_t attn_decode_workspace_size(int batch, int n_q_heads, int n_kv_heads, int 
 }  // extern "C"
 
 namespace {
+
+// Device scratch of attn_decode_noalloc: the partial outputs, maxima,
+// denominators and plan data of one decode call. HIP places a copy of this
+// array on every GPU the library runs on, each at its own address, held until
+// the process ends. Host code never passes the array's name to a kernel (on
+// the host it only stands for the symbol): it looks up the device address of
+// the current GPU's copy once and uses that pointer.
+__device__ __align__(256) unsigned char scratch[ATTN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mutex;
+void *scratch_ptr[kMaxDevices];  // per device id; guarded by scratch_mutex
+
+// Address of the current device's copy of `scratch`, looked up with that
+// device current on its first use, then cached. nullptr if HIP cannot report it.
+void *device_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (scratch_ptr[dev] == nullptr) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+    scratch_ptr[dev] = p;
+  }
+  return scratch_ptr[dev];
+}
 
 int decode_impl(const void *q, const void *k_cache, const void *v_cache, const int32_t *seqlens_k,
                 void *o, float *lse, int n_q_heads, int n_kv_heads, int d, int seqlen_q, int batch,
@@ -304,6 +331,21 @@ int attn_decode(const void *q, const void *k_cache, const void *v_cache, const i
                         batch, max_seqlen_k, workspace, workspace_bytes, stream, 0);
 }
 
+int attn_decode_noalloc(const void *q, const void *k_cache, const void *v_cache, const int32_t *seqlens_k,
+                        void *o, float *lse, int n_q_heads, int n_kv_heads, int d, int seqlen_q, int batch,
+                        int max_seqlen_k, void *stream, int num_splits) {
+  if (!q || !k_cache || !v_cache || !seqlens_k || !o || num_splits < 0) return ATTN_ERR_INVALID;
+  const int st = check_decode_shape(n_q_heads, n_kv_heads, d, seqlen_q, batch, max_seqlen_k);
+  if (st != ATTN_OK) return st;
+  const size_t need = workspace_bytes_for(batch, n_kv_heads, d, plan_pieces(n_kv_heads, d, num_splits),
+                                          decode_cols(n_q_heads, n_kv_heads, seqlen_q));
+  if (need > (size_t)ATTN_NOALLOC_SCRATCH_BYTES) return ATTN_ERR_TOO_LARGE;
+  void *ws = device_scratch();
+  if (ws == nullptr) return ATTN_ERR_DEVICE;
+  return decode_impl(q, k_cache, v_cache, seqlens_k, o, lse, n_q_heads, n_kv_heads, d, seqlen_q, batch,
+                     max_seqlen_k, ws, ATTN_NOALLOC_SCRATCH_BYTES, stream, num_splits, false);
+}
+
 int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int causal,
              int batch, int seqlen_q, int seqlen_k, int n_q_heads, int n_kv_heads, int d,
              void *stream) {
@@ -341,6 +383,7 @@ const char *attn_status_string(int status) {
     case ATTN_ERR_WORKSPACE: return "workspace too small";
     case ATTN_ERR_LAUNCH: return "HIP kernel launch failed";
     case ATTN_ERR_DEVICE: return "no usable HIP device";
+    case ATTN_ERR_TOO_LARGE: return "call needs more than the library's fixed decode scratch (ATTN_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }

@@ -64,6 +64,7 @@ extern "C" {
 #define ATTN_ERR_WORKSPACE (-4)   /* workspace smaller than the plan needs */
 #define ATTN_ERR_LAUNCH (-5)      /* the HIP runtime refused a launch */
 #define ATTN_ERR_DEVICE (-6)      /* no usable HIP device */
+#define ATTN_ERR_TOO_LARGE (-7)   /* needs more than the fixed scratch of attn_decode_noalloc */
 
 /* Largest number of key pieces per KV head a decode plan uses. */
 #define ATTN_MAX_PIECES 4096
@@ -161,6 +162,32 @@ int attn_decode_f16(const void *q, const void *k_cache, const void *v_cache,
                     int n_kv_heads, int d, int seqlen_q, int batch, int max_seqlen_k,
                     void *workspace, size_t workspace_bytes, void *stream,
                     int num_splits);
+
+/* Bytes of the fixed device scratch attn_decode_noalloc works in (32 MiB). */
+#define ATTN_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/*
+ * attn_decode_ex for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, layouts, plan and results as attn_decode_ex (bf16), without
+ * the workspace: the partials live in a fixed library array of
+ * ATTN_NOALLOC_SCRATCH_BYTES on each device, created when the library's code
+ * is loaded on that device and held until the process ends. The call
+ * allocates, frees and memsets nothing; the first call on a device looks up
+ * that device's copy of the array (a symbol lookup, not an allocation).
+ * A call whose plan needs more than the fixed size
+ * (attn_decode_workspace_size(...) > ATTN_NOALLOC_SCRATCH_BYTES, e.g. more
+ * than about 700 sequences with 8 KV heads at d = 128) returns
+ * ATTN_ERR_TOO_LARGE before enqueuing anything. Every call on one device
+ * shares its array, and nothing in it needs clearing (each call writes every
+ * value it later reads): calls whose execution overlaps on one device - on
+ * different streams, or from different host threads without ordering - race
+ * on it and give wrong results; calls ordered on one stream are safe.
+ */
+int attn_decode_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                        const int32_t *seqlens_k, void *o, float *lse, int n_q_heads,
+                        int n_kv_heads, int d, int seqlen_q, int batch, int max_seqlen_k,
+                        void *stream, int num_splits);
 
 /*
  * Prefill forward ([FA4-edges] §Edge 1 · causal masking, §Edge 3 · tile

@@ -33,7 +33,7 @@ def test_library_loads_and_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     ensure_built()
-    for code in (0, -1, -2, -3, -4, -5, -6):
+    for code in (0, -1, -2, -3, -4, -5, -6, -7):
         s = aa.status_string(code)
         assert s and s != "unknown status"
     assert aa.status_string(12345) == "unknown status"
@@ -193,3 +193,23 @@ def test_backward_varlen_validation_and_workspace():
     assert call(ck=ctypes.c_void_p(0x1002)) == aa.ATTN_ERR_MISALIGNED
     assert call(wsb=ws_ok - 1) == aa.ATTN_ERR_WORKSPACE
     assert call(fn=L.attn_bwd_varlen_f16, d=96) == aa.ATTN_ERR_UNSUPPORTED
+
+
+def test_noalloc_decode_validation_before_any_device_work():
+    """attn_decode_noalloc rejects NULL pointers, bad shapes and plans larger than its
+    fixed scratch with no device call (the pointers below are never dereferenced)."""
+    L = ensure_built()
+    p = ctypes.c_void_p(0x10000)
+
+    def call(q, B, Hq, Hkv, d, sq, S, ns=0):
+        return L.attn_decode_noalloc(q, p, p, p, p, None, Hq, Hkv, d, sq, B, S, None, ns)
+
+    assert call(None, 4, 8, 1, 64, 1, 512) == aa.ATTN_ERR_INVALID
+    assert call(p, 4, 8, 3, 64, 1, 512) == aa.ATTN_ERR_INVALID          # Hq % Hkv != 0
+    assert call(p, 4, 8, 1, 96, 1, 512) == aa.ATTN_ERR_UNSUPPORTED      # head size
+    assert call(p, 4, 8, 1, 64, 1, 512, ns=-1) == aa.ATTN_ERR_INVALID
+    big = (2048, 16, 8, 128, 1, 64)
+    assert aa.attn_decode_workspace_size(big[0], big[1], big[2], big[4], big[3], big[5], 0) > \
+        aa.ATTN_NOALLOC_SCRATCH_BYTES
+    assert call(p, 2048, 16, 8, 128, 1, 64) == aa.ATTN_ERR_TOO_LARGE
+    assert call(p, 64, 64, 8, 128, 1, 8192, ns=4096) == aa.ATTN_ERR_TOO_LARGE
