@@ -33,6 +33,8 @@ EXPORTS = ("attn_decode_plan", "attn_decode_workspace_size", "attn_decode", "att
            "attn_bwd_workspace_size", "attn_bwd", "attn_bwd_varlen_workspace_size", "attn_bwd_varlen",
            "attn_bwd_varlen_f16",
            "attn_bwd_f16", "attn_decode_noalloc", "attn_status_string", "attn_version")
+# Every symbol include/attn_probe.h declares (measurement kernels, not the attention path).
+PROBE_EXPORTS = ("attn_probe_stream_read", "attn_probe_mfma_bf16")
 
 _lib = None
 
@@ -82,6 +84,10 @@ def lib() -> ctypes.CDLL:
     for name in ("attn_bwd_varlen", "attn_bwd_varlen_f16"):
         getattr(L, name).argtypes = [vp] * 11 + [i32] * 9 + [vp, sz, vp]
         getattr(L, name).restype = i32
+    L.attn_probe_stream_read.argtypes = [vp, sz, vp, i32, vp]
+    L.attn_probe_stream_read.restype = i32
+    L.attn_probe_mfma_bf16.argtypes = [vp, i32, i32, vp, vp]
+    L.attn_probe_mfma_bf16.restype = i32
     L.attn_status_string.argtypes = [i32]
     L.attn_status_string.restype = ctypes.c_char_p
     L.attn_version.argtypes = []
@@ -345,3 +351,30 @@ def attn_bwd_varlen(q, k, v, o, lse, dout, dq, dk, dv, cu_seqlens_q, cu_seqlens_
             tq, tk, Hq, Hkv, d, _ptr(workspace), wbytes, _stream_ptr(stream))
     if st != ATTN_OK:
         raise AttnError(st, "attn_bwd_varlen")
+
+
+def probe_stream_read(buf, out, grid, stream=None):
+    """Measurement kernel: `grid` work-groups read all of `buf` (contiguous device memory, a
+    multiple of 16 bytes) once; `out` (int32/uint32 device tensor) takes grid * 256 words."""
+    nbytes = buf.numel() * buf.element_size()
+    if not (buf.is_cuda and out.is_cuda and buf.is_contiguous() and out.is_contiguous()):
+        raise ValueError("buf and out must be contiguous device tensors")
+    if out.numel() * out.element_size() < grid * 256 * 4:
+        raise ValueError("out needs grid * 256 words")
+    st = lib().attn_probe_stream_read(_ptr(buf), nbytes, _ptr(out), int(grid), _stream_ptr(stream))
+    if st != 0:
+        raise RuntimeError(f"attn_probe_stream_read failed ({st})")
+
+
+def probe_mfma_bf16(out, grid, iters, clk, stream=None):
+    """Measurement kernel: `grid` work-groups of four waves issue `iters` rounds of four
+    independent bf16 32x32x16 MFMAs each; `out` (float32) takes grid * 256 values, `clk`
+    (int64, 4 entries) the shader and 100 MHz counters at the first wave's start and end."""
+    import torch
+    _check(out, "out", torch.float32)
+    _check(clk, "clk", torch.int64)
+    if out.numel() < grid * 256 or clk.numel() < 4:
+        raise ValueError("out needs grid * 256 floats and clk 4 entries")
+    st = lib().attn_probe_mfma_bf16(_ptr(out), int(grid), int(iters), _ptr(clk), _stream_ptr(stream))
+    if st != 0:
+        raise RuntimeError(f"attn_probe_mfma_bf16 failed ({st})")

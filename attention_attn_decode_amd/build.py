@@ -12,7 +12,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libattn.so")
-SOURCES = ["api.hip", "decode.hip", "fwd.hip", "bwd.hip"]
+SOURCES = ["api.hip", "decode.hip", "fwd.hip", "bwd.hip", "probe.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU forms are disabled for every device compile.

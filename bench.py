@@ -2,26 +2,36 @@
 """Single-GPU benchmark of the attention hot path on MI355X.
 
 A step is one pass of the whole path over one batch of synthetic input:
-  * GQA decode on the headline workload (batch 32, 64 query / 8 KV heads,
-    d = 128, one new token, KV lengths uniform in [1024, 8192]): split-KV
-    kernel + combine, through the C ABI;
+  * GQA decode on every decode workload, each through the C ABI (split-KV
+    kernel + combine): the headline (batch 32, 64 query / 8 KV heads, d = 128,
+    one new token, KV lengths uniform in [1024, 8192]), the small one (batch 1,
+    8/1 heads, d = 64, 512 keys), multi-token decode (batch 16, 32/8 heads,
+    d = 64, 4 causal new tokens over 4096 keys) and long-context decode
+    (batch 4, 32/8 heads, d = 128, 131072 keys);
   * causal prefill (batch 2, 32 heads, d = 128, S = 8192) through attn_fwd;
   * the backward pass of that prefill (dQ, dK, dV from its O and LSE and a
     synthetic dO) through attn_bwd;
   * a packed variable-length causal prefill (16 sequences, lengths uniform in
     [256, 4096], 32 heads, d = 128) through attn_fwd_varlen.
-The headline `value` is decode KV-read bandwidth: algorithmic K+V bytes
-(sum_b L_b * Hkv * 4d) over the measured duration of the decode call, timed
-with HIP events on the stream the kernels run on. Prefill TFLOP/s (exact causal
-FLOPs, 4 d per visible query-key pair) is reported beside it, and backward
-TFLOP/s counted, as the backward page does, as 2.5 times the forward FLOPs.
+Every call is timed with HIP events on the stream its kernels run on. Decode
+inputs rotate over resident copies of at least 1 GiB in total (the Infinity
+Cache is 256 MB), so no call reads K/V that an earlier call left in a cache.
+The headline `value` is the headline decode's KV-read bandwidth: algorithmic
+K+V bytes (sum_b L_b * Hkv * 4d) over the mean duration of its calls. Each
+decode workload reports the same, prefill reports TFLOP/s over the exact
+causal FLOPs (4 d per visible query-key pair), the backward TFLOP/s counted,
+as the backward page does, as 2.5 times the forward FLOPs. After the timed
+steps, two measurement kernels of the library give the device's practical
+ceilings (a streaming read of 2 GiB, a bf16 MFMA loop with its clock), and the
+fp64 CPU oracle is timed on the host (the full headline decode; a sample of
+the prefill).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-backward] [--no-varlen]
 Prints one JSON line.
 
-HBM traffic (roofline.traffic) comes from two rocprofv3 counter passes over
-`bench.py --counter-run` (one 1 GiB device copy for calibration, then one
-decode call, one prefill call and one backward call, nothing timed):
+HBM traffic (`traffic` fields) comes from two rocprofv3 counter passes over
+`bench.py --counter-run` (one 1 GiB device copy for calibration, then one call
+of each decode workload, one prefill and one backward, nothing timed):
   rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT -o fetch -- python bench.py --counter-run
   rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT -o write -- python bench.py --counter-run
   python bench.py --ingest-counters OUT/fetch_counter_collection.csv OUT/write_counter_collection.csv
@@ -86,13 +96,25 @@ def measured_traffic(kernel, src_hash, units):
 
 
 COPY_BYTES = 1 << 30
-TRAFFIC_KERNELS = {  # stored key -> (kernel-name prefixes, sources, workload)
-    "attn_decode": (("decode_stream<", "combine_pieces<"), DECODE_SOURCES,
-                    "gqa-decode b=32 hq=64 hkv=8 d=128 sq=1 kv_len~U[1024,8192] (seed 1001)"),
-    "attn_fwd": (("fwd_persist<", "fwd_pp<"), FWD_SOURCES, "causal-prefill b=2 h=32 d=128 s=8192 (seed 1004)"),
-    "attn_bwd": (("bwd_pre<", "bwd_dkdv<", "bwd_dq<"), BWD_SOURCES,
-                 "causal-prefill backward b=2 h=32 d=128 s=8192 (seed 1004, dO seed 1005)"),
+ROTATION_BYTES = 1 << 30     # each decode workload rotates over resident copies of at least this much K/V
+
+# Decode workloads timed in every step (headline first: it gives `value`).
+DECODE_LEGS = ["gqa-decode", "gqa-decode-small", "multi-token-decode", "long-context-decode"]
+LEG_DESC = {
+    "gqa-decode": "gqa-decode b=32 hq=64 hkv=8 d=128 sq=1 kv_len~U[1024,8192] (seed 1001)",
+    "gqa-decode-small": "gqa-decode-small b=1 hq=8 hkv=1 d=64 sq=1 kv_len=512 (seed 1000)",
+    "multi-token-decode": "multi-token-decode b=16 hq=32 hkv=8 d=64 sq=4 causal kv_len=4096 (seed 1002)",
+    "long-context-decode": "long-context-decode b=4 hq=32 hkv=8 d=128 sq=1 kv_len=131072 (seed 1003)",
 }
+PREFILL_DESC = "causal-prefill b=2 h=32 d=128 s=8192 (seed 1004)"
+BACKWARD_DESC = "causal-prefill backward b=2 h=32 d=128 s=8192 (seed 1004, dO seed 1005)"
+
+# --counter-run dispatch order after the calibration copy: (stored key, kernel-name prefixes of its
+# dispatches in order, sources, workload). Each decode call is a split kernel then one combine kernel.
+COUNTER_LEGS = [(f"attn_decode:{w}", ("decode_stream<", "combine_"), DECODE_SOURCES, LEG_DESC[w]) for w in DECODE_LEGS] + [
+    ("attn_fwd", ("fwd_",), FWD_SOURCES, PREFILL_DESC),
+    ("attn_bwd", ("bwd_pre<", "bwd_dkdv<", "bwd_dq<"), BWD_SOURCES, BACKWARD_DESC),
+]
 
 
 def _short_name(name):
@@ -101,54 +123,75 @@ def _short_name(name):
 
 
 def ingest_counters(fetch_csv, write_csv):
-    """Turn the FETCH_SIZE and WRITE_SIZE passes of `--counter-run` into bytes per launch."""
+    """Turn the FETCH_SIZE and WRITE_SIZE passes of `--counter-run` into bytes per launch.
+
+    The dispatches after the 1 GiB calibration copy are matched, in dispatch order, to the
+    calls `--counter-run` makes (COUNTER_LEGS)."""
     import csv
 
-    def read(path, counter):
-        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
-        copies = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
-        if not copies:
-            raise SystemExit(f"{path}: no copy dispatch to calibrate {counter} against")
-        scale = COPY_BYTES / (max(copies) * 1024.0)   # bytes per counted KiB
-        per = {}
-        for r in rows:
-            per.setdefault(_short_name(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
-        return scale, max(copies), per
+    n_legs = sum(len(prefixes) for _, prefixes, _, _ in COUNTER_LEGS)
 
-    fs, fcopy, fper = read(fetch_csv, "FETCH_SIZE")
-    ws, wcopy, wper = read(write_csv, "WRITE_SIZE")
+    def read(path, counter):
+        # the run ends with the calibration copy followed by the legs' dispatches
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        if len(rows) < n_legs + 1 or "copyBuffer" not in rows[-n_legs - 1]["Kernel_Name"]:
+            raise SystemExit(f"{path}: expected the calibration copy then {n_legs} dispatches at the end")
+        kib = float(rows[-n_legs - 1]["Counter_Value"])
+        seq = [(_short_name(r["Kernel_Name"]), float(r["Counter_Value"])) for r in rows[-n_legs:]]
+        return COPY_BYTES / (kib * 1024.0), kib, seq
+
+    fs, fcopy, fseq = read(fetch_csv, "FETCH_SIZE")
+    ws, wcopy, wseq = read(write_csv, "WRITE_SIZE")
     out = {"note": "HBM bytes per launch: rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch, "
                    "separate passes over bench.py --counter-run), each scaled by the ratio of a "
                    "1 GiB device copy's true bytes to what the same counter read for it.",
            "calibration": {"copy_bytes": COPY_BYTES, "fetch_size_kib": fcopy, "write_size_kib": wcopy,
                            "fetch_scale": round(fs, 4), "write_scale": round(ws, 4)}}
-    for key, (prefixes, srcs, workload) in TRAFFIC_KERNELS.items():
+    i = 0
+    for key, prefixes, srcs, workload in COUNTER_LEGS:
         kern, fetch, write = {}, 0.0, 0.0
-        for nm in fper:
-            if nm.startswith(prefixes):
-                f = statistics.fmean(fper[nm])
-                w = statistics.fmean(wper.get(nm, [0.0]))
-                kern[nm] = {"fetch_kib": round(f, 3), "write_kib": round(w, 3), "dispatches": len(fper[nm])}
-                fetch += f * 1024.0 * fs
-                write += w * 1024.0 * ws
-        if kern:
-            out[key] = {"source_hash": source_hash(srcs), "workload": workload, "kernels": kern,
-                        "fetch_bytes": round(fetch), "write_bytes": round(write),
-                        "bytes_per_launch": round(fetch + write)}
+        for pre in prefixes:
+            if i >= len(fseq) or i >= len(wseq):
+                raise SystemExit(f"counter run ended before {key}")
+            (nf, f), (nw, w) = fseq[i], wseq[i]
+            if not (nf.startswith(pre) and nw == nf):
+                raise SystemExit(f"dispatch {i} after the copy is {nf} / {nw}, expected {pre}... for {key}")
+            kern[nf] = {"fetch_kib": round(f, 3), "write_kib": round(w, 3)}
+            fetch += f * 1024.0 * fs
+            write += w * 1024.0 * ws
+            i += 1
+        out[key] = {"source_hash": source_hash(srcs), "workload": workload, "kernels": kern,
+                    "fetch_bytes": round(fetch), "write_bytes": round(write), "bytes_per_launch": round(fetch + write)}
     with open(COUNTERS, "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
-    print(json.dumps({k: v.get("bytes_per_launch") for k, v in out.items() if isinstance(v, dict)}))
+    print(json.dumps({k: v.get("bytes_per_launch") for k, v in out.items() if isinstance(v, dict) and k != "calibration"}))
+
+
+def host_cores():
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline_decode(x, d):
-    """Time the fp64 oracle on the decode workload (full workload, one pass)."""
+    """Time the fp64 oracle on the full headline decode workload (all host cores for BLAS)."""
     import oracle
-    try:
-        ncores = len(os.sched_getaffinity(0))
-    except AttributeError:
-        ncores = os.cpu_count() or 1
     from threadpoolctl import threadpool_limits
+    ncores = host_cores()
     with threadpool_limits(limits=ncores):
         t0 = time.perf_counter()
         reps = 0
@@ -160,7 +203,133 @@ def cpu_baseline_decode(x, d):
         dt = (time.perf_counter() - t0) / reps
     kv = decode_kv_bytes(x.seqlens, x.k.shape[2], d)
     return {"value": round(kv / dt / 1e9, 3), "unit": "GB/s", "cores": ncores, "kind": "oracle",
-            "sample": f"full decode workload, {reps} pass(es), {dt:.2f} s per pass, numpy fp64"}
+            "cpu_model": cpu_model(),
+            "sample": f"full headline decode workload, {reps} pass(es), {dt:.2f} s per pass, numpy fp64"}
+
+
+def cpu_baseline_prefill(xp):
+    """Time the fp64 oracle on the causal prefill: its (batch, head) pairs on the host
+    threads (BLAS held to one thread each; about 30 s of CPU work in all), in TFLOP/s."""
+    import oracle
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
+    B, S, H, d = xp.q.shape
+    nthr = max(1, min(16, host_cores()))
+    pairs = [(b, h) for b in range(B) for h in range(H)]
+
+    def head(bh):
+        b, h = bh
+        sl = (slice(b, b + 1), slice(None), slice(h, h + 1))
+        oracle.attention(xp.q[sl], xp.k[sl], xp.v[sl], None, True)
+
+    with threadpool_limits(limits=1), ThreadPoolExecutor(nthr) as ex:
+        t0 = time.perf_counter()
+        list(ex.map(head, pairs))
+        dt = time.perf_counter() - t0
+    fl = causal_flops(1, len(pairs), S, d)
+    return {"value": round(fl / dt / 1e12, 4), "unit": "TFLOP/s", "cores": nthr, "kind": "oracle",
+            "cpu_model": cpu_model(),
+            "sample": f"all {len(pairs)} (batch, head) pairs of the causal prefill (S={S}, d={d}) on {nthr} "
+                      f"threads, {dt:.2f} s, numpy fp64"}
+
+
+class DecodeLeg:
+    """One decode workload on the device: q, seqlens, outputs, workspace, and K/V rotated over
+    resident copies of at least ROTATION_BYTES (cache rows past each sequence end are zero)."""
+
+    def __init__(self, aa, wl, name, num_splits, dev, to_dev):
+        import torch
+        self.aa, self.name, self.num_splits = aa, name, num_splits
+        x = wl.decode_inputs(name, pad=wl.BF16_ZERO)
+        B, sq, Hq, d = x.q.shape
+        S, Hkv = x.k.shape[1], x.k.shape[2]
+        self.shape = (B, sq, Hq, Hkv, d, S)
+        self.seqlens = x.seqlens.copy()
+        set_bytes = 2 * x.k.nbytes
+        # at least two sets unless one set alone is at least twice the rotation footprint
+        self.nsets = max(2 if set_bytes < 2 * ROTATION_BYTES else 1, -(-ROTATION_BYTES // set_bytes))
+        self.q = to_dev(x.q)
+        k0 = to_dev(x.k)
+        self.K = torch.empty((self.nsets,) + tuple(k0.shape), dtype=k0.dtype, device=dev)
+        self.K[:] = k0
+        del k0
+        v0 = to_dev(x.v)
+        self.V = torch.empty_like(self.K)
+        self.V[:] = v0
+        del v0, x
+        self.sl = torch.from_numpy(self.seqlens).to(dev)
+        self.o = torch.empty((B, sq, Hq, d), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((B, Hq, sq), dtype=torch.float32, device=dev)
+        self.ws = torch.empty(max(16, aa.attn_decode_workspace_size(B, Hq, Hkv, sq, d, S, num_splits)),
+                              dtype=torch.uint8, device=dev)
+        self.pieces, _ = aa.attn_decode_plan(B, Hq, Hkv, d, sq, S, num_splits)
+        self.kv_bytes = decode_kv_bytes(self.seqlens, Hkv, d)
+        self.ms = []
+
+    def call(self, i, stream):
+        j = i % self.nsets
+        self.aa.attn_decode(self.q, self.K[j], self.V[j], self.sl, self.o, self.lse, workspace=self.ws,
+                            num_splits=self.num_splits, stream=stream)
+
+    def report(self, read_peak):
+        ms = self.ms
+        mean = statistics.fmean(ms)
+        thirds = [ms[k::3] for k in range(3)] if len(ms) >= 3 else [ms]
+        gbps = self.kv_bytes / (mean * 1e-3) / 1e9
+        B, sq, Hq, Hkv, d, S = self.shape
+        r = {"workload": LEG_DESC[self.name], "kernel": "decode_stream + combine", "calls": len(ms),
+             "rotation_sets": self.nsets, "pieces_per_kv_head": self.pieces,
+             "us_mean": round(mean * 1e3, 2), "us_median": round(statistics.median(ms) * 1e3, 2),
+             "us_best_third_median": round(min(statistics.median(t) for t in thirds) * 1e3, 2),
+             "us_min": round(min(ms) * 1e3, 2), "algorithmic_bytes_per_launch": self.kv_bytes,
+             "kv_read_GBps": round(gbps, 1),
+             "problem_GBps": round(decode_problem_bytes(self.seqlens, B, Hq, Hkv, d, sq) / (mean * 1e-3) / 1e9, 1),
+             "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+             "traffic": measured_traffic(f"attn_decode:{self.name}", source_hash(DECODE_SOURCES), None)}
+        if read_peak:
+            r["frac_of_measured_read"] = round(gbps / read_peak, 4)
+        return r
+
+
+def measured_peaks(aa, dev, stream):
+    """Practical ceilings of this device from the library's measurement kernels (not timed steps)."""
+    import torch
+    nbytes = 2 << 30
+    buf = torch.randint(-2 ** 31, 2 ** 31 - 1, (nbytes // 4,), dtype=torch.int32, device=dev)
+    out = torch.empty(4096 * 256, dtype=torch.int32, device=dev)
+    best, best_grid = 0.0, 0
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for grid in (192, 256, 384, 512, 1024, 2048, 4096):
+        for rep in range(3):
+            ev[0].record(stream)
+            aa.probe_stream_read(buf, out, grid, stream)
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            if rep:
+                gb = nbytes / (ev[0].elapsed_time(ev[1]) * 1e-3) / 1e9
+                if gb > best:
+                    best, best_grid = gb, grid
+    del buf, out
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    grid, iters = 2 * cus, 20000
+    outf = torch.empty(grid * 256, dtype=torch.float32, device=dev)
+    clk = torch.zeros(4, dtype=torch.int64, device=dev)
+    tf, ghz = 0.0, 0.0
+    for rep in range(3):
+        ev[0].record(stream)
+        aa.probe_mfma_bf16(outf, grid, iters, clk, stream)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        t = grid * 4 * iters * 4 * 32768 / (ev[0].elapsed_time(ev[1]) * 1e-3) / 1e12
+        c = clk.cpu().tolist()
+        if rep and t > tf:
+            tf, ghz = t, (c[1] - c[0]) / max(1, c[3] - c[2]) * 0.1
+    return {"stream_read_GBps": round(best, 1), "stream_read_grid": best_grid,
+            "stream_read_note": "2 GiB read once by attn_probe_stream_read (16-byte nontemporal loads, 256-thread "
+                                "work-groups), best over grids and repetitions",
+            "mfma_bf16_TFLOPs": round(tf, 1), "mfma_clock_GHz": round(ghz, 3),
+            "mfma_note": f"attn_probe_mfma_bf16: {grid} work-groups x 4 waves, four independent "
+                         "v_mfma_f32_32x32x16_bf16 chains per wave; clock from the shader-clock counter"}
 
 
 def main():
@@ -173,8 +342,10 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-varlen", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true")
     ap.add_argument("--counter-run", action="store_true",
-                    help="one copy, one decode and one prefill dispatch for rocprofv3 --pmc passes")
+                    help="one copy, then one call of each decode workload, one prefill and one backward "
+                         "(for rocprofv3 --pmc passes)")
     ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     args = ap.parse_args()
     if args.ingest_counters:
@@ -204,27 +375,14 @@ def main():
     def to_dev(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
-    # ---- decode workload (cache at capacity, rows past each sequence end zero) ----
-    dc = wl.DECODE_CONFIGS["gqa-decode"]
     t0 = time.perf_counter()
-    xd = wl.decode_inputs(dc, pad=wl.BF16_ZERO)
-    B, sq, Hq, d = xd.q.shape
-    S, Hkv = xd.k.shape[1], xd.k.shape[2]
-    sets = []
-    q0, k0, v0 = to_dev(xd.q), to_dev(xd.k), to_dev(xd.v)
-    sl = torch.from_numpy(xd.seqlens.copy()).to(dev)
-    # two resident copies (2 x 1 GiB of cache) alternate so no step reads
-    # K/V left in the 256 MB Infinity Cache by the previous one
-    sets.append((q0, k0, v0))
-    sets.append((q0.clone(), k0.clone(), v0.clone()))
-    wsz = aa.attn_decode_workspace_size(B, Hq, Hkv, sq, d, S, args.num_splits)
-    ws = torch.empty(wsz, dtype=torch.uint8, device=dev)
-    od = torch.empty((B, sq, Hq, d), dtype=torch.bfloat16, device=dev)
-    lsed = torch.empty((B, Hq, sq), dtype=torch.float32, device=dev)
-    pieces, min_piece = aa.attn_decode_plan(B, Hq, Hkv, d, sq, S, args.num_splits)
+    legs = [DecodeLeg(aa, wl, name, args.num_splits, dev, to_dev) for name in DECODE_LEGS]
+    head = legs[0]
+    xd = wl.decode_inputs("gqa-decode", pad=wl.BF16_ZERO) if not args.no_cpu_baseline else None
 
     # ---- prefill workload ----
     run_prefill = not args.no_prefill
+    xp = None
     if run_prefill:
         pc = wl.PREFILL_CONFIGS["causal-prefill"]
         xp = wl.prefill_inputs(pc)
@@ -237,10 +395,9 @@ def main():
             dqp, dkp, dvp = torch.empty_like(qp), torch.empty_like(kp), torch.empty_like(vp)
             wsb = torch.empty(aa.attn_bwd_workspace_size(pc.batch, pc.n_q_heads, pc.seqlen), dtype=torch.uint8,
                               device=dev)
-        del xp
     else:
         run_backward = False
-    run_varlen = not args.no_varlen
+    run_varlen = not args.no_varlen and not args.counter_run
     if run_varlen:
         xv = wl.varlen_prefill_inputs()
         lens_v = np.diff(xv.cu_q).astype(np.int64)
@@ -252,6 +409,7 @@ def main():
         max_qv = int(lens_v.max())
         varlen_name = xv.meta["config"]
         del xv
+    torch.cuda.synchronize()
     setup_s = time.perf_counter() - t0
 
     stream = torch.cuda.current_stream()
@@ -259,11 +417,12 @@ def main():
     if args.counter_run:
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
+        torch.cuda.synchronize()
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-        q, k, v = sets[0]
-        aa.attn_decode(q, k, v, sl, od, lsed, workspace=ws, num_splits=args.num_splits, stream=stream)
+        for leg in legs:
+            leg.call(0, stream)
         if run_prefill:
             aa.attn_fwd(qp, kp, vp, op, lsep, causal=True, stream=stream)
         if run_backward:
@@ -272,62 +431,63 @@ def main():
         print("counter run done", flush=True)
         return
 
+    # Per step: every decode workload, the prefill, its backward, the packed prefill; an event pair
+    # around each call on the launch stream.
+    nev = len(legs) + 3
+
     def step(i, evs=None):
-        q, k, v = sets[i % 2]
-        if evs:
-            evs[0].record(stream)
-        aa.attn_decode(q, k, v, sl, od, lsed, workspace=ws, num_splits=args.num_splits, stream=stream)
-        if evs:
-            evs[1].record(stream)
+        for li, leg in enumerate(legs):
+            if evs:
+                evs[li][0].record(stream)
+            leg.call(i, stream)
+            if evs:
+                evs[li][1].record(stream)
+        k = len(legs)
         if run_prefill:
+            if evs:
+                evs[k][0].record(stream)
             aa.attn_fwd(qp, kp, vp, op, lsep, causal=True, stream=stream)
-        if evs:
-            evs[2].record(stream)
+            if evs:
+                evs[k][1].record(stream)
         if run_backward:
+            if evs:
+                evs[k + 1][0].record(stream)
             aa.attn_bwd(qp, kp, vp, op, lsep, dop, dqp, dkp, dvp, wsb, causal=True, stream=stream)
-        if evs:
-            evs[3].record(stream)
+            if evs:
+                evs[k + 1][1].record(stream)
         if run_varlen:
+            if evs:
+                evs[k + 2][0].record(stream)
             aa.attn_fwd_varlen(qv, kv_, vv, cqv, ckv, ov, max_qv, lse=lsev, causal=True, stream=stream)
-        if evs:
-            evs[4].record(stream)
+            if evs:
+                evs[k + 2][1].record(stream)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(nev)]
+              for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(args.steps):
-        step(i, events[i])
+        step(args.warmup + i, events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
-    dec_ms = [e[0].elapsed_time(e[1]) for e in events]
-    pre_ms = [e[1].elapsed_time(e[2]) for e in events]
-    bwd_ms = [e[2].elapsed_time(e[3]) for e in events]
-    var_ms = [e[3].elapsed_time(e[4]) for e in events]
-    dec_mean = statistics.fmean(dec_ms)
-    pre_mean = statistics.fmean(pre_ms) if run_prefill else 0.0
+    for li, leg in enumerate(legs):
+        leg.ms = [e[li][0].elapsed_time(e[li][1]) for e in events]
+    k = len(legs)
+    pre_ms = [e[k][0].elapsed_time(e[k][1]) for e in events] if run_prefill else []
+    bwd_ms = [e[k + 1][0].elapsed_time(e[k + 1][1]) for e in events] if run_backward else []
+    var_ms = [e[k + 2][0].elapsed_time(e[k + 2][1]) for e in events] if run_varlen else []
 
-    kv_bytes = decode_kv_bytes(xd.seqlens, Hkv, d)
-    dec_gbps = kv_bytes / (dec_mean * 1e-3) / 1e9
-    prob_gbps = decode_problem_bytes(xd.seqlens, B, Hq, Hkv, d, sq) / (dec_mean * 1e-3) / 1e9
+    peaks = None if args.no_peaks else measured_peaks(aa, dev, stream)
+    read_peak = peaks["stream_read_GBps"] if peaks else None
+    mfma_peak = peaks["mfma_bf16_TFLOPs"] if peaks else None
 
-    # plain device copy for context: practical HBM rate on this part
-    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-    dst = torch.empty_like(src)
-    for _ in range(2):
-        dst.copy_(src)
-    ce = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    ce[0].record(stream)
-    for _ in range(5):
-        dst.copy_(src)
-    ce[1].record(stream)
-    torch.cuda.synchronize()
-    copy_gbps = 5 * 2 * src.numel() / (ce[0].elapsed_time(ce[1]) * 1e-3) / 1e9
-    del src, dst
-
-    dec_hash = source_hash(DECODE_SOURCES)
+    dec = head.report(read_peak)
+    dec_mean_ms = dec["us_mean"] * 1e-3
+    dec_gbps = head.kv_bytes / (statistics.fmean(head.ms) * 1e-3) / 1e9
+    B, sq, Hq, Hkv, d, S = head.shape
     result = {
         "metric": "decode KV-read GB/s (% HBM peak); causal prefill fwd TFLOP/s (% MFMA peak)",
         "value": round(dec_gbps, 2),
@@ -342,13 +502,14 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": "gqa-decode b=32 hq=64 hkv=8 d=128 sq=1 kv_len~U[1024,8192] (seed 1001)",
+            "workload": LEG_DESC["gqa-decode"],
             "global_batch": B,
             "seq_len": int(S),
-            "kv_tokens": int(xd.seqlens.sum()),
-            "pieces_per_kv_head": pieces,
-            "prefill_workload": "causal-prefill b=2 h=32 d=128 s=8192 (seed 1004)" if run_prefill else None,
-            "backward_workload": "backward of that prefill, dO seed 1005" if run_backward else None,
+            "kv_tokens": int(head.seqlens.sum()),
+            "pieces_per_kv_head": head.pieces,
+            "other_decode_workloads": [LEG_DESC[w] for w in DECODE_LEGS[1:]],
+            "prefill_workload": PREFILL_DESC if run_prefill else None,
+            "backward_workload": BACKWARD_DESC if run_backward else None,
             "varlen_workload": varlen_name if run_varlen else None,
             "parallelism": "single-gpu",
             "device": props.name,
@@ -361,27 +522,21 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
-            "traffic": measured_traffic("attn_decode", dec_hash, kv_bytes),
-            "algorithmic_bytes_per_launch": kv_bytes,
-            "avg_launch_ms": round(dec_mean, 5),
+            "traffic": dec["traffic"],
+            "algorithmic_bytes_per_launch": head.kv_bytes,
+            "avg_launch_ms": round(dec_mean_ms, 5),
         },
-        "decode": {
-            "ms_mean": round(dec_mean, 5),
-            "ms_median": round(statistics.median(dec_ms), 5),
-            "ms_min": round(min(dec_ms), 5),
-            "kv_read_GBps": round(dec_gbps, 2),
-            "problem_GBps": round(prob_gbps, 2),
-            "frac_hbm_peak": round(dec_gbps / HBM_PEAK_GBPS, 4),
-            "frac_of_device_copy": round(dec_gbps / copy_gbps, 4),
-        },
-        "device_copy_GBps": round(copy_gbps, 1),
+        "decode": {w: leg.report(read_peak) for w, leg in zip(DECODE_LEGS, legs)},
+        "measured_peaks": peaks,
         "setup_s": round(setup_s, 1),
     }
     if run_prefill:
+        pre_mean = statistics.fmean(pre_ms)
         fl = causal_flops(pc.batch, pc.n_q_heads, pc.seqlen, pc.d)
         tf = fl / (pre_mean * 1e-3) / 1e12
         result["prefill"] = {
             "bound": "mfma",
+            "workload": PREFILL_DESC,
             "kernel": "fwd_persist (dense d = 128: one persistent work-group per CU)",
             "ms_mean": round(pre_mean, 5),
             "ms_median": round(statistics.median(pre_ms), 5),
@@ -390,6 +545,7 @@ def main():
             "peak": BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+            "frac_of_measured_mfma": round(tf / mfma_peak, 4) if mfma_peak else None,
             "traffic": measured_traffic("attn_fwd", source_hash(FWD_SOURCES), None),
         }
     if run_backward:
@@ -398,6 +554,7 @@ def main():
         tf = fl / (bwd_mean * 1e-3) / 1e12
         result["backward"] = {
             "bound": "mfma",
+            "workload": BACKWARD_DESC,
             "kernel": "attn_bwd = bwd_pre + bwd_dkdv + bwd_dq",
             "ms_mean": round(bwd_mean, 5),
             "ms_median": round(statistics.median(bwd_ms), 5),
@@ -407,6 +564,7 @@ def main():
             "peak": BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+            "frac_of_measured_mfma": round(tf / mfma_peak, 4) if mfma_peak else None,
             "traffic": measured_traffic("attn_bwd", source_hash(BWD_SOURCES), None),
         }
     if run_varlen:
@@ -428,6 +586,8 @@ def main():
         }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline_decode(xd, d)
+        if xp is not None:
+            result["cpu_baseline_prefill"] = cpu_baseline_prefill(xp)
     print(json.dumps(result), flush=True)
 
 

@@ -13,11 +13,13 @@ import pytest
 import attention_attn_decode_amd as aa
 from tests._libload import ensure_built
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "attn.h")
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include")
+HEADER = os.path.join(INCLUDE, "attn.h")
+PROBE_HEADER = os.path.join(INCLUDE, "attn_probe.h")
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
 
@@ -29,6 +31,11 @@ def test_library_loads_and_exports_every_declared_symbol():
     for nm in names:
         assert hasattr(L, nm), f"libattn.so does not export {nm}"
     assert sorted(aa.EXPORTS) == names
+    probes = declared_functions(PROBE_HEADER)
+    for nm in probes:
+        assert hasattr(L, nm), f"libattn.so does not export {nm}"
+    assert sorted(aa.PROBE_EXPORTS) == probes
+    assert sorted(os.listdir(INCLUDE)) == ["attn.h", "attn_probe.h"]
 
 
 def test_status_strings_and_version():
@@ -213,3 +220,14 @@ def test_noalloc_decode_validation_before_any_device_work():
         aa.ATTN_NOALLOC_SCRATCH_BYTES
     assert call(p, 2048, 16, 8, 128, 1, 64) == aa.ATTN_ERR_TOO_LARGE
     assert call(p, 64, 64, 8, 128, 1, 8192, ns=4096) == aa.ATTN_ERR_TOO_LARGE
+
+
+def test_probe_validation_before_any_device_work():
+    L = ensure_built()
+    p = ctypes.c_void_p(0x10000)
+    assert L.attn_probe_stream_read(None, 1 << 20, p, 4, None) == -1
+    assert L.attn_probe_stream_read(p, 1000, p, 4, None) == -1          # not a multiple of 16
+    assert L.attn_probe_stream_read(p, 1 << 20, p, 0, None) == -1
+    assert L.attn_probe_mfma_bf16(p, 0, 10, p, None) == -1
+    assert L.attn_probe_mfma_bf16(p, 4, 0, p, None) == -1
+    assert L.attn_probe_mfma_bf16(None, 4, 10, p, None) == -1
