@@ -97,6 +97,21 @@ __device__ __forceinline__ float wave_xor_sum(float x, int mask) {
   return x + __shfl_xor(x, mask, 64);
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave (lane l gets x[0] + ... + x[l],
+// modulo 2^32) through DPP, without LDS: shifts by 1, 2, 4 and 8 lanes within
+// each 16-lane row (lanes shifted in from outside the row add 0), then the last
+// lane of rows 0 and 2 added to rows 1 and 3 (row_bcast:15), then lane 31
+// added to rows 2 and 3 (row_bcast:31).
+__device__ __forceinline__ unsigned wave_incl_scan_u32(unsigned x) {
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2, 3
+  return x;
+}
+
 // Orders this wave's LDS writes before its later LDS reads (and reads before
 // later writes) across lanes: waits for outstanding LDS operations and keeps
 // the compiler from moving memory operations across the point.

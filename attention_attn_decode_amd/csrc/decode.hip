@@ -103,7 +103,8 @@ __device__ long long total_units(const int *lens, int B) {
 // Number of pieces per KV head: the requested P, but no piece shorter than
 // min_units sub-blocks (so tiny inputs do not fan out into empty work).
 __device__ __forceinline__ int pieces_for(long long T, int P, int min_units) {
-  const long long by_len = (T + min_units - 1) / min_units;
+  const long long by_len = T < (1LL << 31) ? (long long)(((unsigned)T + min_units - 1) / (unsigned)min_units)
+                                           : (T + min_units - 1) / min_units;
   return (int)(by_len < P ? (by_len < 1 ? 1 : by_len) : P);
 }
 
@@ -159,6 +160,60 @@ __device__ Seg find_segment(const int *lens, int B, long long x, long long r1) {
   }
   Seg none = {B, 0, 0, 0, carry};
   return none;
+}
+
+// total_units and find_segment for calls whose sub-block counts and their
+// sums over 64 sequences fit in 32 bits (max_len <= 2^25): wave scans through
+// DPP and lane reads instead of LDS shuffles, the running 64-bit carry in
+// scalar registers.
+__device__ long long total_units32(const int *lens, int B) {
+  const int lane = threadIdx.x & 63;
+  long long t = 0;
+  for (int base = 0; base < B; base += 64) {
+    const int b = base + lane;
+    const unsigned n = b < B ? (unsigned)units_of(lens[b]) : 0u;
+    t += __builtin_amdgcn_readlane(wave_incl_scan_u32(n), 63);
+  }
+  return t;
+}
+
+__device__ Seg find_segment32(const int *lens, int B, long long x, long long r1) {
+  const int lane = threadIdx.x & 63;
+  long long carry = 0;
+  for (int base = 0; base < B; base += 64) {
+    const int b = base + lane;
+    const int L = b < B ? lens[b] : 0;
+    const unsigned n = (unsigned)units_of(L);
+    const unsigned incl = wave_incl_scan_u32(n);
+    const long long st = carry + (long long)(incl - n);
+    const unsigned long long hit = __ballot(n > 0 && st <= x && x < st + (long long)n);
+    if (hit) {
+      const int h = __ffsll((long long)hit) - 1;
+      Seg s;
+      s.b = base + h;
+      s.start = carry + (long long)__builtin_amdgcn_readlane(incl - n, h);
+      s.L = __builtin_amdgcn_readlane(L, h);
+      s.lo = (int)(x - s.start) * kSub;
+      s.hi = seg_hi(s.start, s.L, r1);
+      return s;
+    }
+    carry += __builtin_amdgcn_readlane(incl, 63);
+  }
+  Seg none = {B, 0, 0, 0, carry};
+  return none;
+}
+
+// Piece bounds w * T / P_eff and (w + 1) * T / P_eff, in 32-bit arithmetic
+// when the products fit.
+__device__ __forceinline__ void piece_bounds(int w, long long T, int P_eff, long long &r0, long long &r1) {
+  if (T * (long long)P_eff < (1LL << 32)) {
+    const unsigned t = (unsigned)T, p = (unsigned)P_eff;
+    r0 = (unsigned)w * t / p;
+    r1 = (unsigned)(w + 1) * t / p;
+  } else {
+    r0 = piece_begin(w, T, P_eff);
+    r1 = piece_begin(w + 1, T, P_eff);
+  }
 }
 
 // Next non-empty sequence segment before flattened unit r1.
@@ -219,14 +274,17 @@ decode_stream(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int item = blockIdx.x * kWaves + wv;  // = piece * Hkv + kv head
   const int g = item % Hkv, wp = item / Hkv;
-  const long long T = total_units(lens, B);
+  // Sub-block counts and their 64-sequence sums fit in 32 bits below 2^25 keys.
+  const bool plan32 = max_len <= (1 << 25);
+  const long long T = plan32 ? total_units32(lens, B) : total_units(lens, B);
   // The combine step reads the total and every sequence's flattened start
   // from here instead of re-scanning the lengths.
   if (meta != nullptr && item == 0 && lane == 0) meta[0] = T;
   if (T == 0) return;
   const int P_eff = pieces_for(T, P, min_units);
   if (wp >= P_eff) return;
-  const long long r0 = piece_begin(wp, T, P_eff), r1 = piece_begin(wp + 1, T, P_eff);
+  long long r0, r1;
+  piece_bounds(wp, T, P_eff, r0, r1);
 
   const int G = Hq / Hkv, ncol = G * sq;
   const int n = lane & 15, gq = lane >> 4;
@@ -434,7 +492,7 @@ decode_stream(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
     }
   };
 
-  const Seg first = find_segment(lens, B, r0, r1);
+  const Seg first = plan32 ? find_segment32(lens, B, r0, r1) : find_segment(lens, B, r0, r1);
   if (first.b >= B) return;
   const int n_sub = (int)(r1 - r0);  // sub-blocks of this piece
 
