@@ -304,11 +304,11 @@ decode_stream(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
   uint16_t *klds = smem + wv * NTILE * TILE;
   uint16_t *vlds = kOneTile ? klds : klds + TILE;
 
-  // Load one sub-block (sequence b, keys [j0, j0 + 32), valid below hi) into a
-  // ring slot. Rows at or past hi are clamped to hi - 1: every load is issued
-  // unconditionally (a fixed count per sub-block keeps the wait counters exact)
-  // and reads finite data of this sequence, which the mask then excludes.
-  auto load_k = [&](S &sl, int b, int j0, int hi) {
+  // Load one sub-block (sequence b, keys [j0, j0 + 32), valid below hi) into
+  // ring registers. Rows at or past hi are clamped to hi - 1: every load is
+  // issued unconditionally (a fixed count per sub-block keeps the wait counters
+  // exact) and reads finite data of this sequence, which the mask then excludes.
+  auto load_k = [&](auto &sl, int b, int j0, int hi) __attribute__((always_inline)) {
     const uint16_t *kb = kc + ((size_t)b * max_len * Hkv + g) * D;
 #pragma unroll
     for (int qi = 0; qi < NK; ++qi) {
@@ -316,7 +316,7 @@ decode_stream(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
       sl.k[qi] = ld_stream(kb + (size_t)p * rstride + (lane % CH) * 8);
     }
   };
-  auto load_vq = [&](S &sl, int b, int j0, int hi) {
+  auto load_v = [&](auto &sl, int b, int j0, int hi) __attribute__((always_inline)) {
     const uint16_t *vb = vc + ((size_t)b * max_len * Hkv + g) * D;
 #pragma unroll
     for (int hg = 0; hg < NVG; ++hg) {
@@ -327,18 +327,16 @@ decode_stream(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
         sl.v[hg][qq] = ld_stream(vb + (size_t)p * rstride + (lane % CH) * 8);
       }
     }
-    // Q^T B operand of this sequence: slot k of lane group gq at k-step kk
-    // covers chunk 4 * kk + gq of the query row.
+  };
+  // Q^T B operand of sequence b: slot k of lane group gq at k-step kk covers
+  // chunk 4 * kk + gq of the query row.
+  auto load_q = [&](auto &sl, int b) __attribute__((always_inline)) {
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const uint16_t *qrow = q + ((size_t)(b * sq + tn[c]) * Hq + head[c]) * D;
 #pragma unroll
       for (int kk = 0; kk < KST; ++kk) sl.q[c][kk] = ldg16(qrow + (4 * kk + gq) * 8);
     }
-  };
-  auto load_slot = [&](S &sl, int b, int j0, int hi) {
-    load_k(sl, b, j0, hi);
-    load_vq(sl, b, j0, hi);
   };
 
   float m_run[NC], l_run[NC];
@@ -350,32 +348,30 @@ decode_stream(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
     for (int mt = 0; mt < MT; ++mt) oacc[c][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // after_k runs once K is in LDS and after_v once V is (with one tile per
-  // wave): the single-slot pipeline refills the slot's registers there.
-  auto compute_slot = [&](S &sl, const Seg &cs, int j0, bool live, auto &&after_k, auto &&after_v) {
-    // K registers -> LDS (row-major, swizzled chunks).
+  // K registers -> LDS tile (row-major, swizzled chunks).
+  auto store_k = [&](const auto &sl) __attribute__((always_inline)) {
 #pragma unroll
     for (int qi = 0; qi < NK; ++qi) {
       const int r = RPI * qi + lane / CH, c = lane % CH;
       sts16(klds + r * D + ((c ^ k_swz<D>(r)) * 8), sl.k[qi]);
     }
-    // V registers -> LDS (row-major, swizzled chunks).
-    auto store_v = [&]() {
+  };
+  // V registers -> LDS tile (row-major, swizzled chunks).
+  auto store_v = [&](const auto &sl) __attribute__((always_inline)) {
 #pragma unroll
-      for (int hg = 0; hg < NVG; ++hg) {
-        const int g4 = lane / CH + (64 / CH) * hg, c = lane % CH;
+    for (int hg = 0; hg < NVG; ++hg) {
+      const int g4 = lane / CH + (64 / CH) * hg, c = lane % CH;
 #pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
-          const int r = 4 * g4 + qq;
-          sts16(vlds + r * D + ((c ^ v_swz<D>(r)) * 8), sl.v[hg][qq]);
-        }
+      for (int qq = 0; qq < 4; ++qq) {
+        const int r = 4 * g4 + qq;
+        sts16(vlds + r * D + ((c ^ v_swz<D>(r)) * 8), sl.v[hg][qq]);
       }
-    };
-    if constexpr (!kOneTile) store_v();
-    wave_lds_sync();
-    after_k();
-
-    f32x4 sacc[NC][2];
+    }
+  };
+  // S^T = K Q^T of the sub-block whose K is in the LDS tile, with the Q
+  // operand in qs (MFMA row i of tile t is key 8 (i / 4) + 4 t + i % 4).
+  using Scores = f32x4[NC][2];
+  auto scores = [&](const auto &qs, Scores &sacc) __attribute__((always_inline)) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
 #pragma unroll
@@ -387,11 +383,14 @@ decode_stream(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
         const int ck = 4 * kk + gq;
         const uint4 ka = lds16(klds + r * D + ((ck ^ k_swz<D>(r)) * 8));
 #pragma unroll
-        for (int c = 0; c < NC; ++c) sacc[c][t] = mma16<F16>(ka, sl.q[c][kk], sacc[c][t]);
+        for (int c = 0; c < NC; ++c) sacc[c][t] = mma16<F16>(ka, qs.q[c][kk], sacc[c][t]);
       }
     }
-
-    uint4 pop[NC];
+  };
+  // Online softmax of one sub-block's scores: masks, running max and sum,
+  // rescale of O; returns P (element type, the P*V B operand) per group.
+  auto softmax = [&](const Scores &sacc, const Seg &cs, int j0, bool live, uint4 (&pop)[NC])
+                     __attribute__((always_inline)) {
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       // Keys visible to this column: below the segment end and, among the sq
@@ -430,14 +429,10 @@ decode_stream(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
       pop[c] = make_uint4(pack2<F16>(p[0], p[1]), pack2<F16>(p[2], p[3]), pack2<F16>(p[4], p[5]),
                           pack2<F16>(p[6], p[7]));
     }
-    if constexpr (kOneTile) {
-      wave_lds_sync();  // every K read of the score MFMAs has returned
-      store_v();
-      wave_lds_sync();
-      after_v();
-    }
-    // A operand: the same eight keys 8gq .. 8gq + 7 at column 16mt + (lane % 16),
-    // as two transposed 4-key reads.
+  };
+  // O^T += V^T P^T with V in the LDS tile. A operand: the same eight keys
+  // 8gq .. 8gq + 7 at column 16mt + (lane % 16), as two transposed 4-key reads.
+  auto pv = [&](const uint4 (&pop)[NC]) __attribute__((always_inline)) {
     const int trk = lane & 15;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -452,13 +447,12 @@ decode_stream(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
 #pragma unroll
       for (int c = 0; c < NC; ++c) oacc[c][mt] = mma16<F16>(va, pop[c], oacc[c][mt]);
     }
-    wave_lds_sync();
   };
 
   // End of a sequence segment. If the segment is the whole sequence, no other
   // piece touches it: write the final O and LSE. Otherwise write this wave's
   // partial for sequence b to slot wp + b of KV head g. Then reset the state.
-  auto finalize = [&](const Seg &sg) {
+  auto finalize = [&](const Seg &sg) __attribute__((always_inline)) {
     const int b = sg.b;
     if (meta != nullptr && sg.lo == 0 && g == 0 && lane == 0) meta[1 + b] = sg.start;
 #pragma unroll
@@ -496,27 +490,27 @@ decode_stream(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
   if (first.b >= B) return;
   const int n_sub = (int)(r1 - r0);  // sub-blocks of this piece
 
-  // Two ring slots (D <= 128), both explicit: the loads of sub-block i+2 go
-  // into slot A right after sub-block i (slot A) is consumed, while sub-block
-  // i+1 (slot B) is already in flight. Past the last sub-block the load iterator keeps
-  // re-reading the last valid rows and an odd count is padded with one fully
-  // masked sub-block, so the loop body has no data-dependent control flow
-  // around the slots.
-  Seg ls = first;
-  int lj = ls.lo;
-  auto advance_load = [&]() {
-    lj += kSub;
-    if (lj >= ls.hi) {
-      Seg nx = ls;
+  // Sub-block iterators over this piece's segments. A load iterator past the
+  // last sub-block keeps re-reading the last valid rows (its loads are never
+  // used), so the loops below have no data-dependent control flow around the
+  // ring registers.
+  struct Iter {
+    Seg s;
+    int j;
+  };
+  auto advance_load = [&](Iter &it) __attribute__((always_inline)) {
+    it.j += kSub;
+    if (it.j >= it.s.hi) {
+      Seg nx = it.s;
       if (next_segment(nx, lens, B, r1)) {
-        ls = nx;
-        lj = ls.lo;
+        it.s = nx;
+        it.j = it.s.lo;
       }
     }
   };
   Seg cs = first;
   int cj = cs.lo;
-  auto advance_compute = [&]() {
+  auto advance_compute = [&]() __attribute__((always_inline)) {
     cj += kSub;
     if (cj >= cs.hi) {
       finalize(cs);
@@ -524,36 +518,134 @@ decode_stream(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
     }
   };
 
-  auto none = [] {};
   if constexpr (kOneTile) {
-    // One register slot: the next sub-block's K loads are issued as soon as
-    // this one's K is in LDS, its V and Q loads once this one's V is, so they
-    // run under this sub-block's MFMAs (two slots would exceed the register
-    // file at D = 256).
+    // D = 256, one register slot: the next sub-block's K loads are issued as
+    // soon as this one's K is in LDS, its V and Q loads once this one's V is,
+    // so they run under this sub-block's MFMAs (two slots would exceed the
+    // register file). K and V pass through the wave's one LDS tile in turn.
     S r;
-    load_slot(r, ls.b, lj, ls.hi);
-    advance_load();
+    Iter it{first, first.lo};
+    load_k(r, it.s.b, it.j, it.s.hi);
+    load_v(r, it.s.b, it.j, it.s.hi);
+    load_q(r, it.s.b);
+    advance_load(it);
     for (int i = 0; i < n_sub; ++i) {
-      const int nb = ls.b, nj = lj, nhi = ls.hi;
-      compute_slot(r, cs, cj, true, [&] { load_k(r, nb, nj, nhi); }, [&] { load_vq(r, nb, nj, nhi); });
-      advance_load();
+      const int nb = it.s.b, nj = it.j, nhi = it.s.hi;
+      store_k(r);
+      wave_lds_sync();
+      load_k(r, nb, nj, nhi);
+      Scores sacc;
+      scores(r, sacc);
+      uint4 pop[NC];
+      softmax(sacc, cs, cj, true, pop);
+      wave_lds_sync();  // every K read of the score MFMAs has returned
+      store_v(r);
+      wave_lds_sync();
+      load_v(r, nb, nj, nhi);
+      pv(pop);
+      load_q(r, nb);
+      wave_lds_sync();
+      advance_load(it);
       advance_compute();
     }
-  } else {
+  } else if constexpr (NC == 1) {
+    // One column group: two ring slots, each sub-block's K, V and Q together:
+    // sub-block i + 2 is loaded into a slot as soon as sub-block i has left it;
+    // its scores, softmax and P*V run in that order. (Removing all score,
+    // softmax and P*V work speeds these calls by at most 3% - the stream sets
+    // their time - and overlapping scores with softmax, below, made them 1-3%
+    // slower.)
     S ra, rb;
-    load_slot(ra, ls.b, lj, ls.hi);
-    advance_load();
-    load_slot(rb, ls.b, lj, ls.hi);
-    advance_load();
+    Iter it{first, first.lo};
+    auto load_slot = [&](S &sl) __attribute__((always_inline)) {
+      load_k(sl, it.s.b, it.j, it.s.hi);
+      load_v(sl, it.s.b, it.j, it.s.hi);
+      load_q(sl, it.s.b);
+      advance_load(it);
+    };
+    auto compute = [&](S &sl, bool live) __attribute__((always_inline)) {
+      store_k(sl);
+      store_v(sl);
+      wave_lds_sync();
+      Scores sacc;
+      scores(sl, sacc);
+      uint4 pop[NC];
+      softmax(sacc, cs, cj, live, pop);
+      pv(pop);
+      wave_lds_sync();
+    };
+    load_slot(ra);
+    load_slot(rb);
     for (int i = 0; i < n_sub; i += 2) {
-      compute_slot(ra, cs, cj, true, none, none);
-      load_slot(ra, ls.b, lj, ls.hi);
-      advance_load();
+      compute(ra, true);
+      load_slot(ra);
       advance_compute();
       const bool live_b = i + 1 < n_sub;
-      compute_slot(rb, cs, cj, live_b, none, none);
-      load_slot(rb, ls.b, lj, ls.hi);
-      advance_load();
+      compute(rb, live_b);
+      load_slot(rb);
+      if (live_b) advance_compute();
+    }
+  } else {
+    // Two column groups (twice the score, softmax and P*V work per byte: with
+    // that work removed these calls run 11-17% faster): scores of sub-block
+    // i + 1 overlap the softmax of sub-block i ([FA4-decode] §The S/P
+    // Ping-Pong, here between two score register sets of one wave): the score
+    // MFMAs of i + 1 are issued before the exponentials of i, which do not
+    // depend on them, so the matrix unit and the vector ALU work at once. K (with the sequence's Q operand) therefore has to reach LDS
+    // one sub-block before V: K and V have their own two-slot register rings
+    // and load iterators, K running one sub-block ahead, and each ring slot is
+    // refilled (sub-block + 2) as soon as its registers have been used (K once
+    // the score MFMAs have read its Q operand).
+    struct KSlot {
+      uint4 k[NK];
+      uint4 q[NC][KST];
+    };
+    struct VSlot {
+      uint4 v[NVG][4];
+    };
+    KSlot ka, kb;
+    VSlot va, vb;
+    Iter ik{first, first.lo}, iv{first, first.lo};
+    auto load_ks = [&](KSlot &sl) __attribute__((always_inline)) {
+      load_k(sl, ik.s.b, ik.j, ik.s.hi);
+      load_q(sl, ik.s.b);
+      advance_load(ik);
+    };
+    auto load_vs = [&](VSlot &sl) __attribute__((always_inline)) {
+      load_v(sl, iv.s.b, iv.j, iv.s.hi);
+      advance_load(iv);
+    };
+    Scores s_even, s_odd;
+    // Prologue: K of sub-blocks 0 and 1, V of 0 and 1 in flight; scores of 0.
+    load_ks(ka);
+    load_ks(kb);
+    load_vs(va);
+    load_vs(vb);
+    store_k(ka);
+    wave_lds_sync();
+    scores(ka, s_even);
+    wave_lds_sync();
+    load_ks(ka);  // K of sub-block 2
+    // Step i: K(i + 1) (and its Q operand) is in k_next, V(i) in v_cur, the
+    // scores of i in s_cur.
+    auto step = [&](KSlot &k_next, VSlot &v_cur, Scores &s_cur, Scores &s_next, bool live)
+                    __attribute__((always_inline)) {
+      store_k(k_next);
+      store_v(v_cur);
+      wave_lds_sync();
+      load_vs(v_cur);  // V of sub-block i + 2
+      scores(k_next, s_next);
+      load_ks(k_next);  // K of sub-block i + 3, once the scores have taken its Q operand
+      uint4 pop[NC];
+      softmax(s_cur, cs, cj, live, pop);
+      pv(pop);
+      wave_lds_sync();
+    };
+    for (int i = 0; i < n_sub; i += 2) {
+      step(kb, va, s_even, s_odd, true);
+      advance_compute();
+      const bool live_b = i + 1 < n_sub;
+      step(ka, vb, s_odd, s_even, live_b);
       if (live_b) advance_compute();
     }
   }
