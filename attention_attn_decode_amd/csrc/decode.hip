@@ -246,8 +246,16 @@ struct Slot {
 };
 
 // NC column groups of 16 packed query columns (1 or 2); the partial
-// workspace holds 16 * NC columns per slot.
-template <int D, bool F16, int NC>
+// workspace holds 16 * NC columns per slot. GRP selects the work split:
+//   false - balanced pieces: each wave owns one (piece, KV head) of the
+//           flattened sub-blocks of all sequences; sequences spread over
+//           several pieces leave fp32 partials for the combine kernel.
+//   true  - one work-group per (sequence, KV head): its four waves take equal
+//           shares of the sequence's sub-blocks and merge their partials
+//           through LDS, so the call is one kernel with no workspace and no
+//           plan (used when there are enough sequence-head pairs to fill the
+//           chip).
+template <int D, bool F16, int NC, bool GRP>
 __global__ void __launch_bounds__(256, 1)
 decode_stream(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
               const uint16_t *__restrict__ vc, const int *__restrict__ seqlens,
@@ -267,24 +275,47 @@ decode_stream(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
   __shared__ __attribute__((aligned(16))) uint16_t smem[kWaves * NTILE * TILE];
   // Clamped sequence lengths, staged once: segment walks then wait on LDS,
   // never on the vector-memory counter that the K/V stream keeps busy.
-  __shared__ int lens[kMaxBatch];
+  __shared__ int lens[GRP ? 1 : kMaxBatch];
+  // Grouped work-groups: each wave's (max, denominator) per packed column;
+  // the unnormalised outputs go to smem once the stream is done.
+  __shared__ float2 s_ml[GRP ? kWaves * COLS : 1];
+  static_assert(kWaves * COLS * D * sizeof(float) <= sizeof(smem), "merge area exceeds the K/V tiles");
 
-  for (int b = threadIdx.x; b < B; b += blockDim.x) lens[b] = clamp_len(seqlens[b], max_len);
-  __syncthreads();
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int item = blockIdx.x * kWaves + wv;  // = piece * Hkv + kv head
-  const int g = item % Hkv, wp = item / Hkv;
-  // Sub-block counts and their 64-sequence sums fit in 32 bits below 2^25 keys.
-  const bool plan32 = max_len <= (1 << 25);
-  const long long T = plan32 ? total_units32(lens, B) : total_units(lens, B);
-  // The combine step reads the total and every sequence's flattened start
-  // from here instead of re-scanning the lengths.
-  if (meta != nullptr && item == 0 && lane == 0) meta[0] = T;
-  if (T == 0) return;
-  const int P_eff = pieces_for(T, P, min_units);
-  if (wp >= P_eff) return;
-  long long r0, r1;
-  piece_bounds(wp, T, P_eff, r0, r1);
+  int g, wp;
+  long long T = 0, r0 = 0, r1 = 0;
+  int P_eff = 1;
+  Seg first = {0, 0, 0, 0, 0};
+  int n_sub = 0;
+  if constexpr (GRP) {
+    g = blockIdx.x % Hkv;
+    wp = 0;
+    const int b = blockIdx.x / Hkv;
+    const int L = clamp_len(seqlens[b], max_len);
+    const int nu = units_of(L);
+    const int u0 = wv * nu / kWaves, u1 = (wv + 1) * nu / kWaves;
+    first = Seg{b, u0 * kSub, min(u1 * kSub, L), L, 0};
+    n_sub = u1 - u0;  // may be 0 for sequences shorter than four sub-blocks
+  } else {
+    for (int b = threadIdx.x; b < B; b += blockDim.x) lens[b] = clamp_len(seqlens[b], max_len);
+    __syncthreads();
+    const int item = blockIdx.x * kWaves + wv;  // = piece * Hkv + kv head
+    g = item % Hkv;
+    wp = item / Hkv;
+    // Sub-block counts and their 64-sequence sums fit in 32 bits below 2^25 keys.
+    const bool plan32 = max_len <= (1 << 25);
+    T = plan32 ? total_units32(lens, B) : total_units(lens, B);
+    // The combine step reads the total and every sequence's flattened start
+    // from here instead of re-scanning the lengths.
+    if (meta != nullptr && item == 0 && lane == 0) meta[0] = T;
+    if (T == 0) return;
+    P_eff = pieces_for(T, P, min_units);
+    if (wp >= P_eff) return;
+    piece_bounds(wp, T, P_eff, r0, r1);
+    first = plan32 ? find_segment32(lens, B, r0, r1) : find_segment(lens, B, r0, r1);
+    if (first.b >= B) return;
+    n_sub = (int)(r1 - r0);  // sub-blocks of this piece
+  }
 
   const int G = Hq / Hkv, ncol = G * sq;
   const int n = lane & 15, gq = lane >> 4;
@@ -486,10 +517,6 @@ decode_stream(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
     }
   };
 
-  const Seg first = plan32 ? find_segment32(lens, B, r0, r1) : find_segment(lens, B, r0, r1);
-  if (first.b >= B) return;
-  const int n_sub = (int)(r1 - r0);  // sub-blocks of this piece
-
   // Sub-block iterators over this piece's segments. A load iterator past the
   // last sub-block keeps re-reading the last valid rows (its loads are never
   // used), so the loops below have no data-dependent control flow around the
@@ -500,7 +527,7 @@ decode_stream(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
   };
   auto advance_load = [&](Iter &it) __attribute__((always_inline)) {
     it.j += kSub;
-    if (it.j >= it.s.hi) {
+    if (!GRP && it.j >= it.s.hi) {
       Seg nx = it.s;
       if (next_segment(nx, lens, B, r1)) {
         it.s = nx;
@@ -512,12 +539,13 @@ decode_stream(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
   int cj = cs.lo;
   auto advance_compute = [&]() __attribute__((always_inline)) {
     cj += kSub;
-    if (cj >= cs.hi) {
+    if (!GRP && cj >= cs.hi) {
       finalize(cs);
       if (next_segment(cs, lens, B, r1)) cj = cs.lo;
     }
   };
 
+  if (n_sub > 0) {
   if constexpr (kOneTile) {
     // D = 256, one register slot: the next sub-block's K loads are issued as
     // soon as this one's K is in LDS, its V and Q loads once this one's V is,
@@ -647,6 +675,55 @@ decode_stream(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
       const bool live_b = i + 1 < n_sub;
       step(ka, vb, s_odd, s_even, live_b);
       if (live_b) advance_compute();
+    }
+  }
+  }  // n_sub > 0
+
+  if constexpr (GRP) {
+    // Merge the four waves' partials of this (sequence, KV head) through LDS
+    // in wave order (deterministic), then write O and LSE. A wave with no
+    // sub-blocks contributes m = -inf, l = 0, O = 0; an empty sequence thus
+    // gets O = 0 and LSE = -inf.
+    float *s_o = reinterpret_cast<float *>(smem);  // [kWaves][COLS][D]
+    __syncthreads();                               // every wave is done with its K/V tiles
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      float l_col = wave_xor_sum(l_run[c], 16);
+      l_col = wave_xor_sum(l_col, 32);
+      float *dst = s_o + ((size_t)wv * COLS + nc[c]) * D;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) *reinterpret_cast<f32x4 *>(dst + 16 * mt + 4 * gq) = oacc[c][mt];
+      if (gq == 0) s_ml[wv * COLS + nc[c]] = make_float2(m_run[c], l_col);
+    }
+    __syncthreads();
+    constexpr int SEG = D / 16;  // outputs per thread: 16 threads per packed column
+    const int b = first.b;
+    for (int col = threadIdx.x >> 4; col < ncol; col += 16) {
+      const int e0 = (threadIdx.x & 15) * SEG;
+      float M = kNegInf, lsum = 0.f;
+      float acc[SEG];
+#pragma unroll
+      for (int e = 0; e < SEG; ++e) acc[e] = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float2 ml = s_ml[w * COLS + col];
+        if (ml.x == kNegInf) continue;
+        const float Mn = fmaxf(M, ml.x);
+        const float a = exp2_hw(M - Mn), cw = exp2_hw(ml.x - Mn);
+        lsum = lsum * a + ml.y * cw;
+        const float *src = s_o + ((size_t)w * COLS + col) * D + e0;
+#pragma unroll
+        for (int e = 0; e < SEG; ++e) acc[e] = acc[e] * a + src[e] * cw;
+        M = Mn;
+      }
+      const int ct = col / G, chead = g * G + col % G;
+      const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+      uint16_t *dsto = o + ((size_t)(b * sq + ct) * Hq + chead) * D + e0;
+#pragma unroll
+      for (int e = 0; e < SEG; e += 2)
+        *reinterpret_cast<uint32_t *>(dsto + e) = pack2<F16>(acc[e] * inv, acc[e + 1] * inv);
+      if (lse != nullptr && (threadIdx.x & 15) == 0)
+        lse[((size_t)b * Hq + chead) * sq + ct] = lsum > 0.f ? kLn2 * (M + __log2f(lsum)) : kNegInf;
     }
   }
 }
@@ -858,11 +935,27 @@ combine_slices(const float *__restrict__ ws_o, const float2 *__restrict__ ws_ml,
 
 }  // namespace
 
+// Work split of a decode call, from host integers only. One work-group per
+// (sequence, KV head) needs no plan, partials or combine launch, but each pair
+// then streams through a single CU (measured ~33 GB/s for a long pair against
+// 7.2 TB/s for the chip), so it is chosen only where that does not bind:
+// calls with no workspace (where the alternative is one piece per KV head),
+// calls whose whole cache holds at most 256 KB of K/V, and 128 to 512 pairs of
+// at most 512 KB each (measured 5-29% faster there, slower above and below).
+bool use_grouped(int batch, int Hkv, int d, int max_len, bool have_workspace) {
+  if (!have_workspace) return true;
+  const long long pair_bytes = (long long)max_len * 4 * d;  // K and V of one pair at capacity, bf16
+  const long long pairs = (long long)batch * Hkv;
+  if (pairs * pair_bytes <= (256LL << 10)) return true;
+  return pair_bytes <= (512LL << 10) && pairs >= 128 && pairs <= 512;
+}
+
 // Host-side launcher (called by the C ABI after validation). Work-groups:
-// ceil(Hkv * P / 4) for the split kernel (extra waves exit at once when the
-// keys allow fewer pieces); for the combine, B x Hkv when the pieces per
-// sequence are few (P <= kSliceCombine * B), else one per 16-float output
-// slice of every packed column of every (sequence, KV head).
+// B x Hkv for the grouped kernel (no combine); otherwise ceil(Hkv * P / 4)
+// for the split kernel (extra waves exit at once when the keys allow fewer
+// pieces) and, for the combine, B x Hkv when the pieces per sequence are few
+// (P <= kSliceCombine * B), else one per 16-float output slice of every packed
+// column of every (sequence, KV head).
 hipError_t launch_decode(const void *q, const void *k, const void *v, const int32_t *seqlens,
                          void *o, float *lse, float *ws_o, float2 *ws_ml, long long *meta,
                          int batch, int Hq,
@@ -877,23 +970,34 @@ hipError_t launch_decode(const void *q, const void *k, const void *v, const int3
   auto *oo = static_cast<uint16_t *>(o);
   // One column group for up to 16 packed query rows, two for up to 32.
   const bool wide = (Hq / Hkv) * sq > kCols;
+  const bool grouped = use_grouped(batch, Hkv, d, max_len, ws_o != nullptr);
+  const dim3 ggrid((unsigned)((long)batch * Hkv));
   auto split = [&](auto kern) {
-    hipLaunchKernelGGL(kern, grid, block, 0, stream, qq, kk, vv, seqlens, oo, lse, ws_o, ws_ml, meta, batch, Hq,
-                       Hkv, sq, max_len, pieces, min_units, scale_log2);
+    hipLaunchKernelGGL(kern, grouped ? ggrid : grid, block, 0, stream, qq, kk, vv, seqlens, oo, lse, ws_o, ws_ml,
+                       meta, batch, Hq, Hkv, sq, max_len, pieces, min_units, scale_log2);
+  };
+  auto pick = [&](auto kg, auto ks) {
+    if (grouped) split(kg);
+    else split(ks);
   };
   if (d == 256) {
     // One column group only (the C ABI rejects more than 16 packed rows here).
-    if (f16) split(decode_stream<256, true, 1>);
-    else split(decode_stream<256, false, 1>);
+    if (f16) pick(decode_stream<256, true, 1, true>, decode_stream<256, true, 1, false>);
+    else pick(decode_stream<256, false, 1, true>, decode_stream<256, false, 1, false>);
   } else if (d == 128) {
-    if (f16) wide ? split(decode_stream<128, true, 2>) : split(decode_stream<128, true, 1>);
-    else wide ? split(decode_stream<128, false, 2>) : split(decode_stream<128, false, 1>);
+    if (f16) wide ? pick(decode_stream<128, true, 2, true>, decode_stream<128, true, 2, false>)
+                  : pick(decode_stream<128, true, 1, true>, decode_stream<128, true, 1, false>);
+    else wide ? pick(decode_stream<128, false, 2, true>, decode_stream<128, false, 2, false>)
+              : pick(decode_stream<128, false, 1, true>, decode_stream<128, false, 1, false>);
   } else {
-    if (f16) wide ? split(decode_stream<64, true, 2>) : split(decode_stream<64, true, 1>);
-    else wide ? split(decode_stream<64, false, 2>) : split(decode_stream<64, false, 1>);
+    if (f16) wide ? pick(decode_stream<64, true, 2, true>, decode_stream<64, true, 2, false>)
+                  : pick(decode_stream<64, true, 1, true>, decode_stream<64, true, 1, false>);
+    else wide ? pick(decode_stream<64, false, 2, true>, decode_stream<64, false, 2, false>)
+              : pick(decode_stream<64, false, 1, true>, decode_stream<64, false, 1, false>);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
+  if (grouped) return hipSuccess;  // merged in the kernel: no combine step
   // Launched even with one piece per KV head: it writes O = 0 and LSE = -inf
   // for empty sequences, which no split-kernel wave visits.
   if (pieces > kSliceCombine * batch) {

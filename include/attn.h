@@ -132,15 +132,22 @@ size_t attn_decode_workspace_size(int batch, int n_q_heads, int n_kv_heads, int 
  *   (one group: a wave streams its keys through a single register slot
  *   there); batch <= ATTN_MAX_BATCH (else ATTN_ERR_UNSUPPORTED).
  *   workspace / workspace_bytes: caller scratch of at least
- *   attn_decode_workspace_size(...) bytes; workspace == NULL means one piece
- *   per KV head (each sequence is streamed whole by one wave; slow on few
- *   long sequences, but needs no scratch).
+ *   attn_decode_workspace_size(...) bytes; workspace == NULL selects the
+ *   grouped work split below for every shape (slow for few long sequences,
+ *   but needs no scratch).
  *
- * Device work: one split kernel (one work-group of four independent waves per
- * CU, each wave streaming one balanced piece of one KV head), then one combine
- * kernel over (sequence, KV head) that merges the pieces of every sequence
- * spread over several. Both use fp32 arithmetic on partials in a fixed order
- * with no atomics: results are deterministic and bitwise reproducible.
+ * Device work, chosen from the host integers alone:
+ *   - split (the general case): one split kernel (one work-group of four
+ *     independent waves per CU, each wave streaming one balanced piece of one
+ *     KV head), then one combine kernel over (sequence, KV head) that merges
+ *     the pieces of every sequence spread over several;
+ *   - grouped (calls whose whole cache holds at most 256 KB of K/V at
+ *     capacity, or 128 to 512 sequence-head pairs of at most 512 KB each, or no
+ *     workspace): one kernel, one work-group per (sequence, KV head) whose four
+ *     waves share the sequence's keys and merge through LDS; the workspace is
+ *     not touched.
+ * Both use fp32 arithmetic on partials in a fixed order with no atomics:
+ * results are deterministic and bitwise reproducible.
  */
 int attn_decode(const void *q, const void *k_cache, const void *v_cache,
                 const int32_t *seqlens_k, void *o, float *lse, int n_q_heads,

@@ -354,3 +354,29 @@ def test_head_size_256_against_oracle(aa, case):
 def test_head_size_256_f16(aa):
     x = wl.make_decode(3, 16, 2, 256, 1, 3000, [3000, 1234, 5], seed=671, dtype="f16")
     check(aa, x, "d=256 f16")
+
+
+# Shapes the launcher serves with one work-group per (sequence, KV head): whole caches of at most
+# 256 KB of K/V, or 128-512 sequence-head pairs of at most 512 KB each (at capacity). Lengths include
+# empty sequences and sequences shorter than the four 32-key sub-blocks the work-group's waves share.
+GROUPED = [
+    # B, Hq, Hkv, d, sq, max_len, lengths (None = random in [0, max_len]), seed
+    (32, 64, 8, 128, 1, 512, None, 611),
+    (16, 32, 8, 64, 4, 1024, None, 612),
+    (16, 32, 8, 64, 8, 512, None, 613),           # 32 packed rows: two column groups
+    (32, 16, 16, 256, 1, 128, None, 614),         # d = 256, 512 pairs
+    (2, 8, 1, 64, 1, 300, [300, 0], 615),         # tiny call, one empty sequence
+    (1, 8, 1, 64, 1, 512, [97], 616),             # one short sequence: waves 0-3 get 0-1 sub-blocks
+    (128, 8, 1, 128, 2, 512, None, 617),          # 128 pairs, 2 causal new tokens
+]
+
+
+@pytest.mark.parametrize("case", GROUPED, ids=lambda c: f"B{c[0]}h{c[1]}:{c[2]}d{c[3]}sq{c[4]}L{c[5]}")
+def test_grouped_shapes_against_oracle(aa, case):
+    B, Hq, Hkv, d, sq, S, lens, seed = case
+    if lens is None:
+        rng = np.random.default_rng(seed)
+        lens = rng.integers(0, S + 1, size=B)
+        lens[: min(B, 4)] = [0, 1, 33, S][: min(B, 4)]
+    x = wl.make_decode(B, Hq, Hkv, d, sq, S, lens, seed=seed)
+    check(aa, x, f"grouped {case[:6]}")
