@@ -277,16 +277,19 @@ fwd_tile(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
 #pragma unroll
         for (int r = 0; r < 16; ++r) S[t][r] = (32 * t + 16 * (r >> 3) + (r & 7)) < lim ? S[t][r] : kNegInf;
     }
-    float mloc = kNegInf;
+    // Row max and row sum as four independent chains each (a single wave
+    // issues this phase, so one long dependent chain would stall on latency).
+    float mx[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, S[t][r]);
+      for (int r = 0; r < 16; ++r) mx[r & 3] = fmaxf(mx[r & 3], S[t][r]);
+    float mloc = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
     mloc = wave_max_halves(mloc);
     const float mblk = mloc * scale_log2;
     const float m_new = mblk > m_run + kRescaleLog2 ? mblk : m_run;
     const float m_use = m_new == kNegInf ? 0.f : m_new;
-    float psum = 0.f;
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -295,11 +298,12 @@ fwd_tile(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
 #pragma unroll
         for (int s2 = 0; s2 < 8; ++s2) {
           pv8[s2] = exp2_hw(__builtin_fmaf(S[t][8 * hh + s2], scale_log2, -m_use));
-          psum += pv8[s2];
+          ps[s2 & 3] += pv8[s2];
         }
         pop[2 * t + hh] = make_uint4(pack2<F16>(pv8[0], pv8[1]), pack2<F16>(pv8[2], pv8[3]),
                                      pack2<F16>(pv8[4], pv8[5]), pack2<F16>(pv8[6], pv8[7]));
       }
+    const float psum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
     const float alpha = exp2_hw(fmaxf(m_run - m_new, -1e30f));
     l_run = l_run * alpha + psum;
     m_run = m_new;
@@ -319,11 +323,17 @@ fwd_tile(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
   constexpr int NPV = MT * NKS;  // P*V MFMAs per block (= QK MFMAs, NT * KST)
   constexpr int KDEP = 3;
   static_assert(NPV == NT * KST, "both products have the same MFMA count");
+  // At d = 128 the two products alternate MFMA by MFMA (stream slot 2i is
+  // P*V product i, 2i + 1 is score product i), so the transposing V reads and
+  // the plain K reads share the LDS over the whole phase (1% faster); at d = 64
+  // and 256 that keeps both products' registers live at once and spills.
+  constexpr bool PV_QK_INTERLEAVE = D == 128;
   auto pv_qk = [&](int vslot, int kslot, int j) {
     auto rd = [&](int g) {
-      if (g < NPV) return vread(vslot, g / MT, g % MT);
-      const int m = g - NPV;
-      return kread(kslot, m % NT, m / NT);
+      const bool is_pv = PV_QK_INTERLEAVE ? (g % 2 == 0) : (g < NPV);
+      const int i = PV_QK_INTERLEAVE ? g / 2 : (g < NPV ? g : g - NPV);
+      if (is_pv) return vread(vslot, i / MT, i % MT);
+      return kread(kslot, i % NT, i / NT);
     };
     uint4 ring[KDEP];
 #pragma unroll
@@ -341,11 +351,13 @@ fwd_tile(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
         if constexpr (g == 2) store_blk(j + 1 - G);
         if constexpr (g == 6) load_blk(j + 2 - G);
       }
-      if constexpr (g < NPV) {
-        constexpr int ks = g / MT, mt = g % MT;
+      constexpr bool is_pv = PV_QK_INTERLEAVE ? (g % 2 == 0) : (g < NPV);
+      constexpr int i = PV_QK_INTERLEAVE ? g / 2 : (g < NPV ? g : g - NPV);
+      if constexpr (is_pv) {
+        constexpr int ks = i / MT, mt = i % MT;
         oacc[mt] = mma32<F16>(a, pop[ks], oacc[mt]);
       } else {
-        constexpr int m = g - NPV, t = m % NT, kk = m / NT;
+        constexpr int t = i % NT, kk = i / NT;
         if constexpr (kk == 0) S[t] = mma32<F16>(a, qop[kk], f32x16{});
         else S[t] = mma32<F16>(a, qop[kk], S[t]);
       }
