@@ -53,6 +53,8 @@ constexpr int kMaxBatch = 8192;  // sequences per call (lengths staged in LDS)
 // Pieces per sequence (P / B) above which the combine splits each sequence's
 // merge over its output slices instead of one work-group per sequence.
 constexpr int kSliceCombine = 16;
+// Tolerated growth of a column's running max before O is rescaled (base 2).
+constexpr float kRescaleLog2 = 8.f;
 
 // XOR swizzle of the 16-byte chunk index of K row r in the LDS tile [32][D]:
 // the 16 rows one QK A-operand read touches land on 16 distinct bank groups.
@@ -441,22 +443,27 @@ decode_stream(const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
         }
       mloc = wave_xor_max(mloc, 16);
       mloc = wave_xor_max(mloc, 32);
-      // Online softmax in base 2 ([FA4-edges] §The correction).
-      const float m_new = fmaxf(m_run[c], mloc);
+      // Online softmax in base 2 with the conditional rescale ([FA4-edges]
+      // §The correction): the reference max moves only when the sub-block's
+      // max exceeds it by more than kRescaleLog2, so P stays below 2^8 and O
+      // is rescaled only for the few sub-blocks that raise the max that much.
+      const float m_new = mloc > m_run[c] + kRescaleLog2 ? mloc : m_run[c];
       const float m_use = m_new == kNegInf ? 0.f : m_new;
-      const float alpha = exp2_hw(m_run[c] - m_use);
-      float p[8], psum = 0.f;
+      const float alpha = exp2_hw(fmaxf(m_run[c] - m_new, -1e30f));
+      float p[8], ps[2] = {0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         p[i] = exp2_hw(sv[i] - m_use);
-        psum += p[i];
+        ps[i & 1] += p[i];
       }
-      l_run[c] = l_run[c] * alpha + psum;
+      l_run[c] = l_run[c] * alpha + (ps[0] + ps[1]);
       m_run[c] = m_new;
       // Rescale O before accumulating into it ([FA4-edges] §The value MMA waits
-      // on three gates).
+      // on three gates); skipped by the whole wave when no column needs it.
+      if (__any(alpha != 1.f)) {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) oacc[c][mt] *= alpha;
+        for (int mt = 0; mt < MT; ++mt) oacc[c][mt] *= alpha;
+      }
       pop[c] = make_uint4(pack2<F16>(p[0], p[1]), pack2<F16>(p[2], p[3]), pack2<F16>(p[4], p[5]),
                           pack2<F16>(p[6], p[7]));
     }
