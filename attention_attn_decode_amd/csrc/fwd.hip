@@ -55,13 +55,16 @@ template <int D> struct VRow { static constexpr int v = D == 128 ? 160 : 96; };
 //   MFMA phase j: O^T += V(j-1)^T P(j-1)^T, then S(j) = K(j) Q^T (32 MFMAs),
 //                 with the group's share of the K/V staging under them
 //   VALU phase j: softmax of S(j) into P(j) and the rescale of O^T.
-// Group B runs one phase behind group A and every phase ends in a work-group
-// barrier, so on each SIMD one wave issues MFMAs while the other runs its
-// exponentials: the S/P ping-pong of [FA4-decode] §Recap on the FA4 forward
-// pass, played between the two waves of a SIMD instead of two register sets.
-// K and V tiles are shared by all eight waves; group A stages K, group B
-// stages V, each during its MFMA phase, ahead of use (one block through
-// registers at d = 64, two half-steps by direct-to-LDS loads at d = 128).
+// Group B runs one phase behind group A, so on each SIMD one wave issues
+// MFMAs while the other runs its exponentials: the S/P ping-pong of
+// [FA4-decode] §Recap on the FA4 forward pass, played between the two waves
+// of a SIMD instead of two register sets. With direct-to-LDS staging
+// (d >= 128) the groups meet at one work-group barrier per key block (group A
+// runs MFMA(j) then softmax(j), group B softmax(j - 1) then MFMA(j)); with
+// register staging (d = 64) at one per phase. K and V tiles are shared by all
+// eight waves; group A stages K, group B stages V, each during its MFMA phase,
+// ahead of use (one block through registers at d = 64, two half-steps by
+// direct-to-LDS loads at d >= 128).
 constexpr int kBMP = 256;  // query rows per work-group
 // Keys per block: 64, or 32 at d = 256, where a block's score and probability
 // registers must shrink to leave room for the 32-row Q operands and O^T; a
@@ -396,62 +399,99 @@ fwd_tile(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     }
   };
 
-  // Prologue. Register staging: K(0) into slot 0; group A holds K(1), group B
-  // V(0) in registers. Direct loads: K(0) and V(0) into slot 0, then a wait
-  // the compiler sees, so none of its own loads (Q) is pending in the loops.
+  // Direct loads (d >= 128): one barrier per step. Step j is, for group A,
+  // MFMA(j) then softmax(j); for group B, softmax(j - 1) then MFMA(j): within
+  // a step each SIMD's two waves still alternate the matrix unit and the
+  // vector ALU, and the only point where the groups meet is the step's end.
+  // The staging needs nothing more: in step j both groups read K(j) and
+  // V(j - 1); group A loads K(j + 2) into K(j - 1)'s slot and group B V(j + 1)
+  // into V(j - 2)'s, both last read in step j - 1; each wave's wait before the
+  // barrier leaves only the loads it issued in this step in flight, so a block
+  // loaded in step j is complete and published by the end of step j + 1.
   if constexpr (kDma) {
     dma_blk(0);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  } else if (nblk > 0) {
-    if (G == 0) {
-      load_blk(0);
-      store_blk(0);
+    __syncthreads();
+    // The two groups run separate copies of the loop (the order of softmax
+    // and MFMA work differs), so each copy's register assignment only holds
+    // what its own order keeps live across the barrier.
+    auto run = [&](auto grp) {
+      constexpr int GG = decltype(grp)::value;
+      auto step = [&](int j, auto steady) {
+        if constexpr (GG == 1) valu_phase(j - 1);
+        if constexpr (decltype(steady)::value) {
+          __builtin_amdgcn_s_setprio(2);
+          pv_qk(slot_of(j - 1), slot_of(j), j);
+          __builtin_amdgcn_s_setprio(0);
+        } else {
+          mfma_phase(j);
+        }
+        if constexpr (GG == 0) valu_phase(j);
+        dma_wait_one();
+        __syncthreads();
+      };
+      int j = 0;
+      for (; j <= nblk && (j == 0 || j >= nbw); ++j) {  // j = 0, or a wave with nbw <= 1
+        step(j, std::false_type{});
+        if (j == 0 && nbw > 1) {
+          ++j;
+          break;
+        }
+      }
+      for (; j < nbw; ++j) step(j, std::true_type{});
+      for (; j <= nblk; ++j) step(j, std::false_type{});
+    };
+    if (G == 0) run(std::integral_constant<int, 0>{});
+    else run(std::integral_constant<int, 1>{});
+    // Direct loads still in flight (zeros past the last block) land before
+    // the slots are reused.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  } else {
+    // Register staging (d = 64): two barriers per step, one per phase, group B
+    // one phase behind group A. Prologue: K(0) into slot 0; group A holds
+    // K(1), group B V(0) in registers.
+    if (nblk > 0) {
+      if (G == 0) {
+        load_blk(0);
+        store_blk(0);
+      }
+      if (G == 0 && nblk > 1) load_blk(1);
+      if (G == 1) load_blk(0);
     }
-    if (G == 0 && nblk > 1) load_blk(1);
-    if (G == 1) load_blk(0);
-  }
-  __syncthreads();
-  // Group B starts one phase later; both groups pass the same number of
-  // barriers.
-  if (G == 1) __syncthreads();
-  // Steps j = 0 .. nblk. The steady range 1 <= j < nbw, where the MFMA phase
-  // has both products, is a loop of its own, so its register assignment is
-  // not merged with the edge steps'.
-  int j = 0;
-  for (; j <= nblk && (j == 0 || j >= nbw); ++j) {  // j = 0, or a wave with nbw <= 1
-    mfma_phase(j);
-    if (kDma && G == 1) dma_wait_one();
     __syncthreads();
-    valu_phase(j);
-    if (kDma && G == 0) dma_wait_one();
-    __syncthreads();
-    if (j == 0 && nbw > 1) {
-      ++j;
-      break;
+    // Group B starts one phase later; both groups pass the same number of
+    // barriers.
+    if (G == 1) __syncthreads();
+    // Steps j = 0 .. nblk. The steady range 1 <= j < nbw, where the MFMA phase
+    // has both products, is a loop of its own, so its register assignment is
+    // not merged with the edge steps'.
+    int j = 0;
+    for (; j <= nblk && (j == 0 || j >= nbw); ++j) {  // j = 0, or a wave with nbw <= 1
+      mfma_phase(j);
+      __syncthreads();
+      valu_phase(j);
+      __syncthreads();
+      if (j == 0 && nbw > 1) {
+        ++j;
+        break;
+      }
     }
+    for (; j < nbw; ++j) {
+      __builtin_amdgcn_s_setprio(2);
+      pv_qk(slot_of(j - 1), slot_of(j), j);
+      __builtin_amdgcn_s_setprio(0);
+      __syncthreads();
+      valu_phase(j);
+      __syncthreads();
+    }
+    for (; j <= nblk; ++j) {
+      mfma_phase(j);
+      __syncthreads();
+      valu_phase(j);
+      __syncthreads();
+    }
+    if (G == 0) __syncthreads();
   }
-  for (; j < nbw; ++j) {
-    __builtin_amdgcn_s_setprio(2);
-    pv_qk(slot_of(j - 1), slot_of(j), j);
-    __builtin_amdgcn_s_setprio(0);
-    if (kDma && G == 1) dma_wait_one();
-    __syncthreads();
-    valu_phase(j);
-    if (kDma && G == 0) dma_wait_one();
-    __syncthreads();
-  }
-  for (; j <= nblk; ++j) {
-    mfma_phase(j);
-    if (kDma && G == 1) dma_wait_one();
-    __syncthreads();
-    valu_phase(j);
-    if (kDma && G == 0) dma_wait_one();
-    __syncthreads();
-  }
-  // Direct loads still in flight (zeros past the last block) land before
-  // the slots are reused.
-  if constexpr (kDma) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  if (G == 0) __syncthreads();
 
   const float l_col = wave_xor_sum(l_run, 32);
   if (qrow >= Sq) return;
