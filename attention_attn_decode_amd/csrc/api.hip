@@ -1,6 +1,7 @@
 // C ABI of the attention library: argument validation, split planning and
 // kernel launches on the caller's stream. Declarations and the contract of
 // every entry point live in include/attn.h.
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <mutex>
@@ -10,6 +11,24 @@
 #include "attn.h"
 
 namespace attn {
+// Compute units of the current device, queried once per device and cached
+// (256, the MI355X count, if the query fails). Called at launch only, when the
+// caller already uses the device: the host-only plan and workspace calls do
+// not query the device.
+int current_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int ncu = 0;
+  if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0) return 256;
+  if (dev < 64) cache[dev].store(ncu, std::memory_order_relaxed);
+  return ncu;
+}
+
 hipError_t launch_decode(const void *q, const void *k, const void *v, const int32_t *seqlens,
                          void *o, float *lse, float *ws_o, float2 *ws_ml, long long *meta,
                          int batch, int Hq,

@@ -558,6 +558,8 @@ fwd_persist(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
 
 }  // namespace
 
+int current_cus();  // compute units of the current device (cached; api.hip)
+
 // Dense when cu_q == nullptr (Sq, Sk the per-sequence lengths); packed
 // variable-length otherwise (Sq = the longest query length, which sizes the
 // grid; Sk unused; total_q, total_k the packed row counts).
@@ -577,10 +579,7 @@ hipError_t launch_fwd(const void *q, const void *k, const void *v, void *o, floa
                        Hq, Hkv, causal, scale_log2, n_mblocks, BH);
   };
   if (d == 128 && cu_q == nullptr) {
-    int dev = 0, ncu = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0)
-      return hipErrorInvalidDevice;
+    const int ncu = current_cus();
     const int nwg = ntiles < ncu ? ntiles : ncu;
     if (f16) run(fwd_persist<128, true>, nwg);
     else run(fwd_persist<128, false>, nwg);
