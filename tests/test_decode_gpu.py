@@ -111,6 +111,35 @@ def test_needles_at_block_and_split_boundaries(aa, d):
     G.assert_parity(o, lse, O_ref, L_ref, "needles")
 
 
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("pattern", ["ramp", "steps", "descending"])
+def test_rising_running_max(aa, d, pattern):
+    """Scores that climb along the sequence (a ramp, or jumps of 3-12 in base 2
+    every 96 keys) move each column's running max many times, by more and by
+    less than the rescale threshold, inside pieces, across piece boundaries and
+    in the grouped kernel; a descending ramp never moves it after the first
+    sub-block. Keys j get k = c_j * q + noise, so s_j grows with c_j."""
+    L, B = 1500, 3
+    x = wl.make_decode(B, 4, 4, d, 1, 1536, [L, L - 37, L - 700], seed=71 + d)
+    rng = np.random.default_rng(7 + d)
+    j = np.arange(L, dtype=np.float64)
+    if pattern == "ramp":
+        c = 3.0 * j / L
+    elif pattern == "steps":
+        c = np.cumsum(np.where(j % 96 == 95, rng.uniform(3.0, 12.0, L), 0.0)) / np.sqrt(d) / np.log2(np.e)
+    else:
+        c = 3.0 * (1.0 - j / L)
+    for b in range(B):
+        for h in range(4):
+            qf = oracle.bf16_bits_to_f64(x.q[b, 0, h])
+            noise = rng.normal(0.0, 0.3, (L, d))
+            x.k[b, :L, h] = wl.f32_to_bf16_bits((c[:, None] * qf[None, :] + noise).astype(np.float32))
+    O_ref, L_ref = oracle.attention(x.q, x.k, x.v, x.seqlens, True)
+    for ns, ws in ((0, "auto"), (1, "auto"), (7, "auto"), (0, None)):
+        o, lse = run_decode(aa, x, num_splits=ns, workspace=ws)
+        G.assert_parity(o, lse, O_ref, L_ref, f"{pattern} d={d} splits={ns} ws={'none' if ws is None else 'yes'}")
+
+
 def test_future_needle_is_masked_for_earlier_tokens(aa):
     """sq = 4: key L-1 is visible only to the last new token (bottom-right)."""
     L, sq = 1000, 4
