@@ -90,46 +90,22 @@ __device__ __forceinline__ int tile_off(int r, int chunk) {
 // A operand of a product contracting over the tile's rows: lane (m, h) of
 // 16-row step ks, M-tile mt gets rows 16 ks + 8 h .. +7 of column 32 mt + m,
 // assembled from two transposing reads (rows +0..3 and +4..7).
-//
-// X selects, at D = 128 (256-byte rows, tiles 256-byte aligned), the forward's
-// address form: a lane base XOR a constant plus a constant (the swizzle of row
-// r depends on r % 16 only, and the chunk bits that mt or kk select do not
-// overlap the lane's). It keeps one address register per read pattern but
-// costs an add and an XOR per read: the dQ kernel takes it (it then holds 234
-// registers without a spill, 0.8% faster), the dK/dV kernel, whose steps are
-// bound by vector-instruction issue, keeps precomputed addresses.
-template <int D, bool X = false>
+template <int D>
 __device__ __forceinline__ uint4 tile_tr_operand(const uint16_t *tile, int lane, int ks, int mt) {
   const int k = lane & 15, half = (lane >> 4) & 1, hl = lane >> 5;
-  if constexpr (D == 128 && X) {
-    const int cl = 2 * half + ((k & 3) >> 1), ra = 8 * hl + (k >> 2);
-    const unsigned ta = 256u * ra + 16u * (cl ^ chunk_swz<D>(ra)) + 8u * (k & 1);
-    const unsigned tb = 256u * (ra + 4) + 16u * (cl ^ chunk_swz<D>(ra + 4)) + 8u * (k & 1);
-    const unsigned base = lds_offset(tile);
-    const uint2 a = lds_tr4_at(((base + ta) ^ (64u * mt)) + 4096u * ks);
-    const uint2 b = lds_tr4_at(((base + tb) ^ (64u * mt)) + 4096u * ks);
-    return make_uint4(a.x, a.y, b.x, b.y);
-  } else {
-    const int c = 4 * mt + 2 * half + ((k & 3) >> 1);
-    const int r0 = 16 * ks + 8 * hl + (k >> 2);
-    const uint2 a = lds_tr4(tile + tile_off<D>(r0, c) + 4 * (k & 1));
-    const uint2 b = lds_tr4(tile + tile_off<D>(r0 + 4, c) + 4 * (k & 1));
-    return make_uint4(a.x, a.y, b.x, b.y);
-  }
+  const int c = 4 * mt + 2 * half + ((k & 3) >> 1);
+  const int r0 = 16 * ks + 8 * hl + (k >> 2);
+  const uint2 a = lds_tr4(tile + tile_off<D>(r0, c) + 4 * (k & 1));
+  const uint2 b = lds_tr4(tile + tile_off<D>(r0 + 4, c) + 4 * (k & 1));
+  return make_uint4(a.x, a.y, b.x, b.y);
 }
 
 // A operand of a product contracting over d: lane (n, h) of 32-row tile t,
 // k-step kk gets row 32 t + pi(n), elements 16 kk + 8 h .. +7.
-template <int D, bool X = false>
+template <int D>
 __device__ __forceinline__ uint4 tile_row_operand(const uint16_t *tile, int lane, int t, int kk) {
-  if constexpr (D == 128 && X) {
-    const int pr = pi_row(lane & 31), hl = lane >> 5;
-    const unsigned lb = 256u * pr + 16u * (hl ^ chunk_swz<D>(pr));
-    return lds16_at(((lds_offset(tile) + lb) ^ (32u * kk)) + 8192u * t);
-  } else {
-    const int r = 32 * t + pi_row(lane & 31);
-    return lds16(tile + tile_off<D>(r, 2 * kk + (lane >> 5)));
-  }
+  const int r = 32 * t + pi_row(lane & 31);
+  return lds16(tile + tile_off<D>(r, 2 * kk + (lane >> 5)));
 }
 
 // ---------------------------------------------------------------------------
@@ -480,7 +456,7 @@ bwd_dq(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uin
   constexpr int KTL = kKB * D;          // one K (or V) tile, elements
   constexpr int NTH = kDqThreads<D>, QTL = kQT<D>;
   constexpr int LPT = kKB * CH / NTH;   // 16-byte chunks per thread per tile
-  __shared__ __attribute__((aligned(256))) uint16_t smem[2 * 2 * KTL];  // {K, V} x 2 slots
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * KTL];  // {K, V} x 2 slots
 
   const int x = blockIdx.x;
   const int qt_ = n_qtiles - 1 - x / BH;  // last query tile first: the longest key range under a causal mask
@@ -599,7 +575,7 @@ bwd_dq(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uin
         mfma_stream<4 * KST, 3>(
             [&](auto gc) {
               constexpr int g = decltype(gc)::value, t = g / (2 * KST), kk = (g / 2) % KST;
-              return tile_row_operand<D, true>(g % 2 ? vtl : ktl, lane, t, kk);
+              return tile_row_operand<D>(g % 2 ? vtl : ktl, lane, t, kk);
             },
             [&](auto gc, const uint4 &a) {
               constexpr int g = decltype(gc)::value, t = g / (2 * KST), kk = (g / 2) % KST;
@@ -613,8 +589,8 @@ bwd_dq(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uin
           for (int r = 0; r < 16; ++r) S[t][r] = 0.f, dP[t][r] = 0.f;
 #pragma unroll
           for (int kk = 0; kk < KST; ++kk) {
-            S[t] = mma32<F16>(tile_row_operand<D, true>(ktl, lane, t, kk), qop[kk], S[t]);
-            dP[t] = mma32<F16>(tile_row_operand<D, true>(vtl, lane, t, kk), doop[kk], dP[t]);
+            S[t] = mma32<F16>(tile_row_operand<D>(ktl, lane, t, kk), qop[kk], S[t]);
+            dP[t] = mma32<F16>(tile_row_operand<D>(vtl, lane, t, kk), doop[kk], dP[t]);
           }
         }
       }
@@ -655,7 +631,7 @@ bwd_dq(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uin
         mfma_stream<4 * MT, 3>(
             [&](auto gc) {
               constexpr int g = decltype(gc)::value;
-              return tile_tr_operand<D, true>(ktl, lane, g % 4, g / 4);
+              return tile_tr_operand<D>(ktl, lane, g % 4, g / 4);
             },
             [&](auto gc, const uint4 &a) {
               constexpr int g = decltype(gc)::value;
@@ -665,7 +641,7 @@ bwd_dq(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uin
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-          for (int ks = 0; ks < 4; ++ks) dqT[mt] = mma32<F16>(tile_tr_operand<D, true>(ktl, lane, ks, mt), pS[ks], dqT[mt]);
+          for (int ks = 0; ks < 4; ++ks) dqT[mt] = mma32<F16>(tile_tr_operand<D>(ktl, lane, ks, mt), pS[ks], dqT[mt]);
       }
     }
     __builtin_amdgcn_s_setprio(0);
