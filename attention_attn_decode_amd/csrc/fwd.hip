@@ -552,7 +552,12 @@ fwd_persist(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     if (x < ntiles)
       fwd_tile<D, F16>(q, k, v, o, lse, cu_q, cu_k, total_q, total_k, Sq, Sk, Hq, Hkv, causal, scale_log2, n_mblocks,
                        BH, (int)x, smem);
-    __syncthreads();  // the next tile's prologue rewrites the LDS slots
+    // The next tile's prologue rewrites the LDS slots: every wave must be
+    // past its last LDS read and its direct loads must have landed (each wave
+    // waited for its own before leaving the tile). The tile's O and LSE stores
+    // need not complete first (the next tile reads other memory), so this is
+    // a bare barrier, not a release fence that would wait for them.
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   }
 }
 
