@@ -8,20 +8,22 @@
 // Same inner loop as decode, widened: S^T = K Q^T and O^T = V^T P^T with
 // v_mfma_f32_32x32x16_bf16, each wave owning 32 query columns. A work-group
 // of eight waves owns a 256-row query tile and shares 64-key K and V tiles
-// in LDS (two slots each). K and V stay row-major in LDS (padded rows, 16-byte
-// writes); the P*V operand, which needs keys along its k dimension, is read
-// with the transposing ds_read_b64_tr_b16.
+// in LDS (32-key tiles at d = 256): three slots each of dense, chunk-swizzled
+// rows filled by direct-to-LDS loads at d >= 128, two slots of padded rows
+// filled through registers at d = 64. K and V stay row-major in LDS; the P*V
+// operand, which needs keys along its k dimension, is read with the
+// transposing ds_read_b64_tr_b16.
 //
 // Causal masking ([FA4-edges] §Edge 1 · causal masking): per (query strip,
 // key block) the block is fully visible, on the diagonal (masked to -inf
 // before the max), or skipped; a work-group only walks keys [0, kend) and a
 // wave skips the math of blocks entirely in its future.
-// Scheduling ([FA4-edges] §Edge 3 · tile scheduling): work-groups are
-// numbered heaviest first (last query tile first, longest visible key range),
-// a longest-processing-time order that shortens the tail. With batch * heads a
-// multiple of 8, all query tiles of one (batch, head) fall on the same XCD
-// (work-groups are dealt round-robin to the 8 XCDs), so they share K/V in that
-// XCD's L2.
+// Scheduling ([FA4-edges] §Edge 3 · tile scheduling): tiles are numbered
+// heaviest first (last query tile first, longest visible key range), a
+// longest-processing-time order that shortens the tail. With batch * heads a
+// multiple of 8, the tiles of one (batch, head) that run at the same time fall
+// on one XCD (work-groups are dealt round-robin to the 8 XCDs), where they
+// share that pair's K/V in the XCD's L2.
 //
 // Key order inside a 32-key score tile: MFMA row i holds key pi(i), where pi
 // swaps bits 2 and 3 of i. Lane half h (= lane / 32) then finds, in registers

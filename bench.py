@@ -36,8 +36,9 @@ of each decode workload, one prefill and one backward, nothing timed):
   rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT -o write -- python bench.py --counter-run
   python bench.py --ingest-counters OUT/fetch_counter_collection.csv OUT/write_counter_collection.csv
 The last step (no GPU) scales each counter by what it read for the copy and
-stores bytes per launch, keyed by a hash of the kernel sources, in
-profiles/hbm_traffic_counters.json; a stale hash reports traffic as null.
+stores bytes per launch, keyed by a hash of the kernel code (comments and
+layout excluded), in profiles/hbm_traffic_counters.json; a stale hash reports
+traffic as null.
 """
 from __future__ import annotations
 
@@ -60,11 +61,37 @@ BWD_SOURCES = ["attention_attn_decode_amd/csrc/bwd.hip", "attention_attn_decode_
 COUNTERS = os.path.join(ROOT, "profiles", "hbm_traffic_counters.json")
 
 
+def _code_only(text):
+    """C/C++ source with comments removed and whitespace runs collapsed (string and
+    character literals kept as written), so that comment edits do not count as a
+    change of the kernel."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def source_hash(paths):
+    """Hash of the kernels' code (comments and layout excluded)."""
     h = hashlib.sha256()
     for p in paths:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
