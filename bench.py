@@ -125,7 +125,8 @@ def measured_traffic(kernel, src_hash, units):
 COPY_BYTES = 1 << 30
 ROTATION_BYTES = 1 << 30     # each decode workload rotates over resident copies of at least this much K/V
 
-# Decode workloads timed in every step (headline first: it gives `value`).
+# Decode workloads timed in every step; the first (the headline) gives `value`
+# and runs last in the step.
 DECODE_LEGS = ["gqa-decode", "gqa-decode-small", "multi-token-decode", "long-context-decode"]
 LEG_DESC = {
     "gqa-decode": "gqa-decode b=32 hq=64 hkv=8 d=128 sq=1 kv_len~U[1024,8192] (seed 1001)",
