@@ -374,10 +374,11 @@ fwd_tile(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
   // last read in the previous half-step) and loads K(j+2); group B, half a
   // step later, writes V(j) (into V(j-2)'s slot) and loads V(j+1). Each tile
   // is visible one barrier before its first reader.
-  // With direct loads (three slots), group A loads K(j+2) in its phase j
-  // into the slot K(j-1) held, last read in the previous half-step, and group
-  // B loads V(j+1) into the slot of V(j-2): two half-steps of lead. A block
-  // past the last loads zeros into a slot nobody reads again.
+  // With direct loads (three slots), group A loads K(j+2) in step j into the
+  // slot K(j-1) held and group B loads V(j+1) into the slot of V(j-2), both
+  // last read before the barrier that ended step j-1; each block is complete
+  // and published one barrier before its first reader. A block past the last
+  // loads zeros into a slot nobody reads again.
   auto stage = [&](int j) {
     if constexpr (kDma) {
       if (G == 0 && j == 0) dma_blk(1);
