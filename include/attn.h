@@ -88,7 +88,7 @@ extern "C" {
  * by that worker; a sequence spread over several pieces is merged by the
  * combine step. This call reports the host side of that plan: `pieces`, the
  * number of pieces per KV head (num_splits = 0 asks for the automatic value,
- * ceil(W / n_kv_heads) with W = 1024 workers for d = 64 and 896 for d = 128,
+ * ceil(W / n_kv_heads) with W = 1024 workers for d = 64 and 896 for d >= 128,
  * about one work-group of four waves per CU on a 256-CU part, as measured best
  * for HBM streaming; a positive value is honoured up to ATTN_MAX_PIECES) and
  * `min_piece`.
