@@ -561,6 +561,8 @@ def main():
         },
         "decode": {w: leg.report(read_peak) for w, leg in zip(DECODE_LEGS, legs)},
         "measured_peaks": peaks,
+        "timing": ("plain launches (no graph), each call bracketed by HIP events on its own stream; "
+                   "means over the timed steps; decode K/V rotated over >= 1 GiB of resident copies"),
         "setup_s": round(setup_s, 1),
     }
     if run_prefill:
