@@ -141,8 +141,12 @@ fwd_tile(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
   if (kend < 0) kend = 0;
   const int nblk = (kend + BN - 1) / BN;
   const int bound = row_bound(qrow);
-  const int wave_lo = row_bound(r0), wave_hi = row_bound(r0 + 31);
-  const int nbw = min(nblk, (wave_hi + BN - 1) / BN);  // blocks this wave computes
+  // Blocks this wave computes: up to its last row inside the sequence; none
+  // when all its rows lie past Sq (the last tile of a sequence), whose
+  // results are never stored (the wave still stages its share and meets
+  // every barrier).
+  const int wave_lo = row_bound(r0), wave_hi = row_bound(min(r0 + 31, Sq - 1));
+  const int nbw = r0 >= Sq ? 0 : min(nblk, (wave_hi + BN - 1) / BN);
 
   uint4 qop[KST];
   {
