@@ -13,9 +13,15 @@ A step is one pass of the whole path over one batch of synthetic input:
     synthetic dO) through attn_bwd;
   * a packed variable-length causal prefill (16 sequences, lengths uniform in
     [256, 4096], 32 heads, d = 128) through attn_fwd_varlen.
-Every call is timed with HIP events on the stream its kernels run on. Decode
-inputs rotate over resident copies of at least 1 GiB in total (the Infinity
-Cache is 256 MB), so no call reads K/V that an earlier call left in a cache.
+Each workload's calls are captured once in a HIP graph and the steps replay
+the graphs, one pair of HIP events around each replay on the stream the
+kernels run on: a decode graph holds a few back-to-back calls (CALLS_PER_REPLAY),
+the prefill, backward and packed-prefill graphs one call each, and a call's
+time is its replay's time over its call count. Decode inputs rotate over
+resident copies of at least 1 GiB in total (the Infinity Cache is 256 MB), so
+no call reads K/V that an earlier call left in a cache. After the timed steps
+every workload is also timed as plain launches, an event pair around each call
+(`*_plain` fields), which adds the event markers' cost to every call.
 The headline `value` is the headline decode's KV-read bandwidth: algorithmic
 K+V bytes (sum_b L_b * Hkv * 4d) over the mean duration of its calls. Each
 decode workload reports the same, prefill reports TFLOP/s over the exact
@@ -124,6 +130,11 @@ def measured_traffic(kernel, src_hash, units):
 
 COPY_BYTES = 1 << 30
 ROTATION_BYTES = 1 << 30     # each decode workload rotates over resident copies of at least this much K/V
+# Back-to-back calls per graph replay (a replay costs ~10 us before its first kernel, spread over its
+# calls). Calls cycle through the K/V copies, so between two reads of one copy at least 0.6 GB of other
+# K/V is read (more than twice the 256 MB Infinity Cache).
+CALLS_PER_REPLAY = {"gqa-decode": 8, "gqa-decode-small": 32, "multi-token-decode": 16, "long-context-decode": 4}
+PLAIN_CALLS = 8              # plain-launch calls per workload after the timed steps
 
 # Decode workloads timed in every step; the first (the headline) gives `value`
 # and runs last in the step.
@@ -294,12 +305,29 @@ class DecodeLeg:
                               dtype=torch.uint8, device=dev)
         self.pieces, _ = aa.attn_decode_plan(B, Hq, Hkv, d, sq, S, num_splits)
         self.kv_bytes = decode_kv_bytes(self.seqlens, Hkv, d)
-        self.ms = []
+        self.ms, self.ms_plain, self.reps, self.graphs = [], [], 1, []
 
     def call(self, i, stream):
         j = i % self.nsets
         self.aa.attn_decode(self.q, self.K[j], self.V[j], self.sl, self.o, self.lse, workspace=self.ws,
                             num_splits=self.num_splits, stream=stream)
+
+    def capture(self, cap_stream, nreplays):
+        """Graphs of `reps` back-to-back calls; graph g reads K/V copies g * reps + r (mod the copy count),
+        so with many small copies every replay of the run reads copies no earlier replay touched."""
+        import torch
+        self.reps = CALLS_PER_REPLAY[self.name]
+        ngraphs = max(1, min(-(-self.nsets // self.reps), nreplays))
+        self.graphs = []
+        for gi in range(ngraphs):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap_stream):
+                for r in range(self.reps):
+                    self.call(gi * self.reps + r, cap_stream)
+            self.graphs.append(g)
+
+    def replay(self, i):
+        self.graphs[i % len(self.graphs)].replay()
 
     def report(self, read_peak):
         ms = self.ms
@@ -307,7 +335,8 @@ class DecodeLeg:
         thirds = [ms[k::3] for k in range(3)] if len(ms) >= 3 else [ms]
         gbps = self.kv_bytes / (mean * 1e-3) / 1e9
         B, sq, Hq, Hkv, d, S = self.shape
-        r = {"workload": LEG_DESC[self.name], "kernel": "decode_stream + combine", "calls": len(ms),
+        r = {"workload": LEG_DESC[self.name], "kernel": "decode_stream + combine", "calls": len(ms) * self.reps,
+             "calls_per_replay": self.reps, "graphs": len(self.graphs),
              "rotation_sets": self.nsets, "pieces_per_kv_head": self.pieces,
              "us_mean": round(mean * 1e3, 2), "us_median": round(statistics.median(ms) * 1e3, 2),
              "us_best_third_median": round(min(statistics.median(t) for t in thirds) * 1e3, 2),
@@ -316,6 +345,8 @@ class DecodeLeg:
              "problem_GBps": round(decode_problem_bytes(self.seqlens, B, Hq, Hkv, d, sq) / (mean * 1e-3) / 1e9, 1),
              "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
              "traffic": measured_traffic(f"attn_decode:{self.name}", source_hash(DECODE_SOURCES), None)}
+        if self.ms_plain:
+            r["us_mean_plain"] = round(statistics.fmean(self.ms_plain) * 1e3, 2)
         if read_peak:
             r["frac_of_measured_read"] = round(gbps / read_peak, 4)
         return r
@@ -461,37 +492,55 @@ def main():
         print("counter run done", flush=True)
         return
 
-    # Per step: the prefill, its backward, the packed prefill, then every decode workload, the headline
-    # last; an event pair around each call on the launch stream. The steps are enqueued without waiting,
-    # so the host runs ahead of the device and no call's start event fires on an idle queue before the
-    # call itself is launched - except the first call after the synchronize that opens the timed region,
-    # which is therefore the long prefill (its host launch gap is then a fraction of a percent of it).
-    nev = len(legs) + 3
+    # Each workload's calls as a graph (one eager call of each first, outside any capture). Per step: the
+    # prefill, its backward, the packed prefill, then every decode workload, the headline last; one event
+    # pair around each replay on the launch stream. The steps are enqueued without waiting, so the host
+    # runs ahead of the device and no replay's start event fires on an idle queue before the replay itself
+    # is launched - except the first after the synchronize that opens the timed region, which is therefore
+    # the long prefill (its host launch gap is then a fraction of a percent of it).
+    def run_prefill_call(s):
+        aa.attn_fwd(qp, kp, vp, op, lsep, causal=True, stream=s)
+
+    def run_backward_call(s):
+        aa.attn_bwd(qp, kp, vp, op, lsep, dop, dqp, dkp, dvp, wsb, causal=True, stream=s)
+
+    def run_varlen_call(s):
+        aa.attn_fwd_varlen(qv, kv_, vv, cqv, ckv, ov, max_qv, lse=lsev, causal=True, stream=s)
+
+    single = [f for f, on in ((run_prefill_call, run_prefill), (run_backward_call, run_backward),
+                              (run_varlen_call, run_varlen)) if on]
+    for f in single:
+        f(stream)
+    for leg in legs:
+        leg.call(0, stream)
+    torch.cuda.synchronize()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(stream)
+    nreplays = args.warmup + args.steps
+    for leg in legs:
+        leg.capture(cap, nreplays)
+    single_graphs = []
+    for f in single:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            f(cap)
+        single_graphs.append(g)
+    stream.wait_stream(cap)
+    torch.cuda.synchronize()
+    nev = len(legs) + len(single_graphs)
 
     def step(i, evs=None):
         k = len(legs)
-        if run_prefill:
+        for si, g in enumerate(single_graphs):
             if evs:
-                evs[k][0].record(stream)
-            aa.attn_fwd(qp, kp, vp, op, lsep, causal=True, stream=stream)
+                evs[k + si][0].record(stream)
+            g.replay()
             if evs:
-                evs[k][1].record(stream)
-        if run_backward:
-            if evs:
-                evs[k + 1][0].record(stream)
-            aa.attn_bwd(qp, kp, vp, op, lsep, dop, dqp, dkp, dvp, wsb, causal=True, stream=stream)
-            if evs:
-                evs[k + 1][1].record(stream)
-        if run_varlen:
-            if evs:
-                evs[k + 2][0].record(stream)
-            aa.attn_fwd_varlen(qv, kv_, vv, cqv, ckv, ov, max_qv, lse=lsev, causal=True, stream=stream)
-            if evs:
-                evs[k + 2][1].record(stream)
+                evs[k + si][1].record(stream)
         for li in reversed(range(len(legs))):
             if evs:
                 evs[li][0].record(stream)
-            legs[li].call(i, stream)
+            legs[li].replay(i)
             if evs:
                 evs[li][1].record(stream)
 
@@ -507,11 +556,29 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     for li, leg in enumerate(legs):
-        leg.ms = [e[li][0].elapsed_time(e[li][1]) for e in events]
+        leg.ms = [e[li][0].elapsed_time(e[li][1]) / leg.reps for e in events]
     k = len(legs)
-    pre_ms = [e[k][0].elapsed_time(e[k][1]) for e in events] if run_prefill else []
-    bwd_ms = [e[k + 1][0].elapsed_time(e[k + 1][1]) for e in events] if run_backward else []
-    var_ms = [e[k + 2][0].elapsed_time(e[k + 2][1]) for e in events] if run_varlen else []
+    single_ms = [[e[k + si][0].elapsed_time(e[k + si][1]) for e in events] for si in range(len(single_graphs))]
+    pre_ms = single_ms.pop(0) if run_prefill else []
+    bwd_ms = single_ms.pop(0) if run_backward else []
+    var_ms = single_ms.pop(0) if run_varlen else []
+
+    # The same calls as plain launches, an event pair around each (not part of the timed steps).
+    def plain(f, n):
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n)]
+        for c in range(n):
+            ev[c][0].record(stream)
+            f(c)
+            ev[c][1].record(stream)
+        torch.cuda.synchronize()
+        return [e[0].elapsed_time(e[1]) for e in ev]
+
+    plain_ms = {}
+    for f, name in zip(single, [n for n, on in (("prefill", run_prefill), ("backward", run_backward),
+                                                 ("varlen_prefill", run_varlen)) if on]):
+        plain_ms[name] = plain(lambda c, f=f: f(stream), 3)
+    for leg in reversed(legs):
+        leg.ms_plain = plain(lambda c, leg=leg: leg.call(c, stream), PLAIN_CALLS)
 
     peaks = None if args.no_peaks else measured_peaks(aa, dev, stream)
     read_peak = peaks["stream_read_GBps"] if peaks else None
@@ -561,8 +628,11 @@ def main():
         },
         "decode": {w: leg.report(read_peak) for w, leg in zip(DECODE_LEGS, legs)},
         "measured_peaks": peaks,
-        "timing": ("plain launches (no graph), each call bracketed by HIP events on its own stream; "
-                   "means over the timed steps; decode K/V rotated over >= 1 GiB of resident copies"),
+        "timing": ("HIP graph replays: each workload's calls captured once (decode: calls_per_replay back-to-back "
+                   "calls per replay, K/V rotated over >= 1 GiB of resident copies; prefill, backward, packed "
+                   "prefill: one call), one pair of HIP events around each replay on the launch stream; a call's "
+                   "time = replay time / calls per replay; means over the timed steps. *_plain: the same calls "
+                   "as plain launches with an event pair around each, after the timed steps"),
         "setup_s": round(setup_s, 1),
     }
     if run_prefill:
@@ -575,6 +645,7 @@ def main():
             "kernel": "fwd_persist (dense d = 128: one persistent work-group per CU)",
             "ms_mean": round(pre_mean, 5),
             "ms_median": round(statistics.median(pre_ms), 5),
+            "ms_mean_plain": round(statistics.fmean(plain_ms["prefill"]), 5),
             "flops": fl,
             "achieved": round(tf, 2),
             "peak": BF16_PEAK_TFLOPS,
@@ -593,6 +664,7 @@ def main():
             "kernel": "attn_bwd = bwd_pre + bwd_dkdv + bwd_dq",
             "ms_mean": round(bwd_mean, 5),
             "ms_median": round(statistics.median(bwd_ms), 5),
+            "ms_mean_plain": round(statistics.fmean(plain_ms["backward"]), 5),
             "flops": int(fl),
             "flops_note": "2.5 x the causal forward FLOPs (five products per visible pair)",
             "achieved": round(tf, 2),
@@ -612,6 +684,7 @@ def main():
             "kernel": "fwd_pp (packed offsets, one work-group per tile)",
             "ms_mean": round(var_mean, 5),
             "ms_median": round(statistics.median(var_ms), 5),
+            "ms_mean_plain": round(statistics.fmean(plain_ms["varlen_prefill"]), 5),
             "tokens": int(lens_v.sum()),
             "flops": fl,
             "achieved": round(tf, 2),

@@ -207,8 +207,9 @@ def test_fwd_page_correctness_config_in_its_dtype(aa):
 
 def test_prefill_graph_replay_without_memset(aa):
     """Captured prefill calls (the persistent d = 128 grid, whose launch reads
-    the CU count, and the packed d = 64 path), replayed with new queries; each
-    replay must equal an eager call on the same inputs and match the oracle."""
+    the CU count, and the packed path at d = 64 and d = 128), replayed with new
+    queries; each replay must equal an eager call on the same inputs and match
+    the oracle."""
     torch = G.torch()
     B, S, Hq, Hkv, d = 1, 700, 4, 2, 128
     x = wl.make_prefill(B, Hq, Hkv, d, S, S, seed=151)
@@ -220,12 +221,18 @@ def test_prefill_graph_replay_without_memset(aa):
     cq, ck = G.dev_i32(xv.cu_q), G.dev_i32(xv.cu_k)
     ov = G.nan_like_bf16(qv.shape)
     lv = G.nan_f32((qv.shape[1], qv.shape[0]))
+    xw = wl.make_varlen([260, 513], [260, 600], 4, 2, 128, seed=157)
+    qw, kw, vw = G.dev_bf16(xw.q), G.dev_bf16(xw.k), G.dev_bf16(xw.v)
+    cqw, ckw = G.dev_i32(xw.cu_q), G.dev_i32(xw.cu_k)
+    ow = G.nan_like_bf16(qw.shape)
+    lw = G.nan_f32((qw.shape[1], qw.shape[0]))
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
 
     def calls(stream):
         aa.attn_fwd(q, k, v, o, lse, causal=True, stream=stream)
         aa.attn_fwd_varlen(qv, kv, vv, cq, ck, ov, 300, lse=lv, causal=True, stream=stream)
+        aa.attn_fwd_varlen(qw, kw, vw, cqw, ckw, ow, 513, lse=lw, causal=True, stream=stream)
 
     with torch.cuda.stream(s):
         calls(s)  # warm-up outside capture
@@ -241,12 +248,16 @@ def test_prefill_graph_replay_without_memset(aa):
         g.replay()
         torch.cuda.synchronize()
         og, lg, ovg, lvg = G.host_f64(o), G.host_f64(lse), G.host_f64(ov), G.host_f64(lv)
+        owg, lwg = G.host_f64(ow), G.host_f64(lw)
         o2, l2 = G.nan_like_bf16((B, S, Hq, d)), G.nan_f32((B, Hq, S))
         aa.attn_fwd(q, k, v, o2, l2, causal=True)
         ov2, lv2 = G.nan_like_bf16(qv.shape), G.nan_f32((qv.shape[1], qv.shape[0]))
         aa.attn_fwd_varlen(qv, kv, vv, cq, ck, ov2, 300, lse=lv2, causal=True)
+        ow2, lw2 = G.nan_like_bf16(qw.shape), G.nan_f32((qw.shape[1], qw.shape[0]))
+        aa.attn_fwd_varlen(qw, kw, vw, cqw, ckw, ow2, 513, lse=lw2, causal=True)
         torch.cuda.synchronize()
         assert np.array_equal(og, G.host_f64(o2)) and np.array_equal(lg, G.host_f64(l2)), f"dense replay {rep}"
         assert np.array_equal(ovg, G.host_f64(ov2)) and np.array_equal(lvg, G.host_f64(lv2)), f"packed replay {rep}"
+        assert np.array_equal(owg, G.host_f64(ow2)) and np.array_equal(lwg, G.host_f64(lw2)), f"packed d=128 {rep}"
         O_ref, L_ref = oracle.attention(xq.q, x.k, x.v, None, True)
         G.assert_parity(og, lg, O_ref, L_ref, f"prefill graph replay {rep}")
