@@ -11,7 +11,7 @@
 //   dV = P^T dO,  dK = s dS^T Q,  dQ = s dS K,  D = rowsum(dO o O).
 //
 // Three kernels, no atomics and no zero-initialised memory:
-//   bwd_pre   D and L * log2(e) per query row, into the caller's workspace.
+//   bwd_pre   -D and L * log2(e) per query row, into the caller's workspace.
 //   bwd_dkdv  one work-group per (batch, KV head, key tile), as in the page's
 //             recap: it owns its K and V rows, walks the query tiles of every
 //             query head that reads its KV head (GQA heads summed in
@@ -109,8 +109,9 @@ __device__ __forceinline__ uint4 tile_row_operand(const uint16_t *tile, int lane
 }
 
 // ---------------------------------------------------------------------------
-// D = rowsum(dO o O) and L2 = L * log2(e) (+inf for a row that sees no key)
-// per (batch, head, query) row, rows padded to Sq_pad with D = 0, L2 = +inf.
+// -D = -rowsum(dO o O) and L2 = L * log2(e) (+inf for a row that sees no key)
+// per (batch, head, query) row, rows padded to Sq_pad with -D = 0, L2 = +inf.
+// D is stored negated: bwd_dkdv starts its dP accumulators from it.
 template <int D>
 __global__ void __launch_bounds__(256)
 bwd_pre(const uint16_t *__restrict__ o, const uint16_t *__restrict__ dout, const float *__restrict__ lse,
@@ -148,7 +149,7 @@ bwd_pre(const uint16_t *__restrict__ o, const uint16_t *__restrict__ dout, const
 #pragma unroll
     for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, LPR);
     if (sub == 0) {
-      dws[row] = i < Sq ? acc : 0.f;
+      dws[row] = i < Sq ? -acc : 0.f;
       l2ws[row] = l2;
     }
   }
@@ -313,7 +314,19 @@ bwd_dkdv(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const u
       // runs at raised priority, so the other's softmax work fills the gaps
       // instead of competing with it.
       __builtin_amdgcn_s_setprio(2);
+      // dP starts from -D (stored negated by bwd_pre), so the MFMAs leave
+      // dP - D and dS = P o dP needs no subtraction.
       f32x16 S, dP;
+      {
+        const float *dpn = &stat[st & 1][1][8 * hl];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const float4 na = *reinterpret_cast<const float4 *>(dpn + 16 * hf);
+          const float4 nb = *reinterpret_cast<const float4 *>(dpn + 16 * hf + 4);
+          dP[8 * hf + 0] = na.x, dP[8 * hf + 1] = na.y, dP[8 * hf + 2] = na.z, dP[8 * hf + 3] = na.w;
+          dP[8 * hf + 4] = nb.x, dP[8 * hf + 5] = nb.y, dP[8 * hf + 6] = nb.z, dP[8 * hf + 7] = nb.w;
+        }
+      }
       if constexpr (kOperandRing<D> && !kVinLds) {
         // S^T = K Q^T and dP^T = V dO^T as one stream (Q and dO rows from LDS).
         mfma_stream<2 * KST, 3>(
@@ -324,11 +337,11 @@ bwd_dkdv(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const u
             [&](auto gc, const uint4 &a) {
               constexpr int g = decltype(gc)::value, kk = g / 2;
               if constexpr (g % 2 == 0) S = mma32<F16>(a, kop[kk], kk == 0 ? f32x16{} : S);
-              else dP = mma32<F16>(a, vop[kk], kk == 0 ? f32x16{} : dP);
+              else dP = mma32<F16>(a, vop[kk], dP);
             });
       } else {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) S[r] = 0.f, dP[r] = 0.f;
+        for (int r = 0; r < 16; ++r) S[r] = 0.f;
 #pragma unroll
         for (int kk = 0; kk < KST; ++kk) {
           S = mma32<F16>(tile_row_operand<D>(qt, lane, 0, kk), kop[kk], S);
@@ -341,7 +354,6 @@ bwd_dkdv(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const u
       __builtin_amdgcn_s_setprio(0);
       // Register r holds query i0 + 16 (r / 8) + 8 hl + r % 8.
       const float *l2p = &stat[st & 1][0][8 * hl];
-      const float *dp = &stat[st & 1][1][8 * hl];
       const int lim = causal ? key - off : -0x40000000;  // query i sees this key iff i >= lim
       uint4 pP[2], pS[2];
       {
@@ -361,16 +373,13 @@ bwd_dkdv(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const u
           float pv[8], sv[8];
           const float4 la = *reinterpret_cast<const float4 *>(l2p + 16 * hf);
           const float4 lb = *reinterpret_cast<const float4 *>(l2p + 16 * hf + 4);
-          const float4 da = *reinterpret_cast<const float4 *>(dp + 16 * hf);
-          const float4 db = *reinterpret_cast<const float4 *>(dp + 16 * hf + 4);
           const float lh[8] = {la.x, la.y, la.z, la.w, lb.x, lb.y, lb.z, lb.w};
-          const float dh[8] = {da.x, da.y, da.z, da.w, db.x, db.y, db.z, db.w};
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const int r = 8 * hf + e;
             const float p = exp2_hw(__builtin_fmaf(S[r], scale_log2, -lh[e]));
             pv[e] = p;
-            sv[e] = p * (dP[r] - dh[e]);
+            sv[e] = p * dP[r];
           }
           pP[hf] = make_uint4(pack2<F16>(pv[0], pv[1]), pack2<F16>(pv[2], pv[3]), pack2<F16>(pv[4], pv[5]),
                               pack2<F16>(pv[6], pv[7]));
@@ -493,7 +502,7 @@ bwd_dq(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uin
   // reads), so every read stays inside the sequence's statistics.
   const int qs = min(qrow, Sq - 1);
   const float l2 = l2ws[stat_b + (size_t)h * Sq_pad + qs];
-  const float Dr = dws[stat_b + (size_t)h * Sq_pad + qs];
+  const float nDr = dws[stat_b + (size_t)h * Sq_pad + qs];  // -D
   f32x16 dqT[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
@@ -617,7 +626,7 @@ bwd_dq(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uin
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
               const int r = 8 * hf + e;
-              sv8[e] = exp2_hw(__builtin_fmaf(S[t][r], scale_log2, -l2)) * (dP[t][r] - Dr);
+              sv8[e] = exp2_hw(__builtin_fmaf(S[t][r], scale_log2, -l2)) * (dP[t][r] + nDr);
             }
             pS[2 * t + hf] = make_uint4(pack2<F16>(sv8[0], sv8[1]), pack2<F16>(sv8[2], sv8[3]),
                                         pack2<F16>(sv8[4], sv8[5]), pack2<F16>(sv8[6], sv8[7]));

@@ -254,8 +254,8 @@ int attn_fwd_varlen_f16(const void *q, const void *k, const void *v, const int32
 
 /*
  * Bytes of workspace attn_bwd needs: 2 * batch * n_q_heads * Sq_pad * 4 with
- * Sq_pad = seqlen_q rounded up to a multiple of 128 (a base-2 LSE and the row
- * sum D per query row). No initialisation is needed. Returns 0 for invalid
+ * Sq_pad = seqlen_q rounded up to a multiple of 128 (a base-2 LSE and the
+ * negated row sum D per query row). No initialisation is needed. Returns 0 for invalid
  * arguments. Host-only.
  */
 size_t attn_bwd_workspace_size(int batch, int n_q_heads, int seqlen_q);
