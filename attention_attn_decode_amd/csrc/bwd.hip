@@ -503,6 +503,12 @@ bwd_dq(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uin
   const int qs = min(qrow, Sq - 1);
   const float l2 = l2ws[stat_b + (size_t)h * Sq_pad + qs];
   const float nDr = dws[stat_b + (size_t)h * Sq_pad + qs];  // -D
+  // At d = 64 the dP MFMAs start from -D (the lane's query row), so dS = P o dP
+  // needs no addition; at d = 128 the 16 registers are not free.
+  constexpr bool kFoldD = D == 64;
+  f32x16 ndv;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) ndv[r] = nDr;
   f32x16 dqT[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
@@ -589,7 +595,7 @@ bwd_dq(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uin
             [&](auto gc, const uint4 &a) {
               constexpr int g = decltype(gc)::value, t = g / (2 * KST), kk = (g / 2) % KST;
               if constexpr (g % 2 == 0) S[t] = mma32<F16>(a, qop[kk], kk == 0 ? f32x16{} : S[t]);
-              else dP[t] = mma32<F16>(a, doop[kk], kk == 0 ? f32x16{} : dP[t]);
+              else dP[t] = mma32<F16>(a, doop[kk], kk == 0 ? (kFoldD ? ndv : f32x16{}) : dP[t]);
             });
       } else {
 #pragma unroll
@@ -626,7 +632,7 @@ bwd_dq(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uin
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
               const int r = 8 * hf + e;
-              sv8[e] = exp2_hw(__builtin_fmaf(S[t][r], scale_log2, -l2)) * (dP[t][r] + nDr);
+              sv8[e] = exp2_hw(__builtin_fmaf(S[t][r], scale_log2, -l2)) * (kFoldD ? dP[t][r] : dP[t][r] + nDr);
             }
             pS[2 * t + hf] = make_uint4(pack2<F16>(sv8[0], sv8[1]), pack2<F16>(sv8[2], sv8[3]),
                                         pack2<F16>(sv8[4], sv8[5]), pack2<F16>(sv8[6], sv8[7]));
