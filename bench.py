@@ -131,8 +131,8 @@ def measured_traffic(kernel, src_hash, units):
 COPY_BYTES = 1 << 30
 ROTATION_BYTES = 1 << 30     # each decode workload rotates over resident copies of at least this much K/V
 # Back-to-back calls per graph replay (a replay costs ~10 us before its first kernel, spread over its
-# calls). Calls cycle through the K/V copies, so between two reads of one copy at least 0.6 GB of other
-# K/V is read (more than twice the 256 MB Infinity Cache).
+# calls). Calls cycle through the K/V copies (replay_plan), so between two reads of the same K/V bytes
+# the run reads at least 1 GB of K/V, four times the 256 MB Infinity Cache.
 CALLS_PER_REPLAY = {"gqa-decode": 8, "gqa-decode-small": 32, "multi-token-decode": 16, "long-context-decode": 4}
 PLAIN_CALLS = 8              # plain-launch calls per workload after the timed steps
 
@@ -274,6 +274,20 @@ def cpu_baseline_prefill(xp):
                       f"threads, {dt:.2f} s, numpy fp64"}
 
 
+def rotation_sets(set_bytes):
+    """Resident K/V copies of one decode workload (one copy = K and V at capacity): at least
+    ROTATION_BYTES in total, and at least two unless one copy alone is twice that."""
+    return max(2 if set_bytes < 2 * ROTATION_BYTES else 1, -(-ROTATION_BYTES // set_bytes))
+
+
+def replay_plan(nsets, reps, nreplays):
+    """K/V copy each call of each captured graph reads: call r of graph g reads copy (g * reps + r) mod
+    nsets, with as many graphs as it takes to visit every copy once but no more than the run's replays
+    (replay i runs graph i mod the graph count)."""
+    ngraphs = max(1, min(-(-nsets // reps), nreplays))
+    return [[(g * reps + r) % nsets for r in range(reps)] for g in range(ngraphs)]
+
+
 class DecodeLeg:
     """One decode workload on the device: q, seqlens, outputs, workspace, and K/V rotated over
     resident copies of at least ROTATION_BYTES (cache rows past each sequence end are zero)."""
@@ -288,7 +302,7 @@ class DecodeLeg:
         self.seqlens = x.seqlens.copy()
         set_bytes = 2 * x.k.nbytes
         # at least two sets unless one set alone is at least twice the rotation footprint
-        self.nsets = max(2 if set_bytes < 2 * ROTATION_BYTES else 1, -(-ROTATION_BYTES // set_bytes))
+        self.nsets = rotation_sets(set_bytes)
         self.q = to_dev(x.q)
         k0 = to_dev(x.k)
         self.K = torch.empty((self.nsets,) + tuple(k0.shape), dtype=k0.dtype, device=dev)
@@ -313,17 +327,15 @@ class DecodeLeg:
                             num_splits=self.num_splits, stream=stream)
 
     def capture(self, cap_stream, nreplays):
-        """Graphs of `reps` back-to-back calls; graph g reads K/V copies g * reps + r (mod the copy count),
-        so with many small copies every replay of the run reads copies no earlier replay touched."""
+        """Graphs of back-to-back calls over the K/V copies replay_plan assigns them."""
         import torch
         self.reps = CALLS_PER_REPLAY[self.name]
-        ngraphs = max(1, min(-(-self.nsets // self.reps), nreplays))
         self.graphs = []
-        for gi in range(ngraphs):
+        for sets in replay_plan(self.nsets, self.reps, nreplays):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=cap_stream):
-                for r in range(self.reps):
-                    self.call(gi * self.reps + r, cap_stream)
+                for j in sets:
+                    self.call(j, cap_stream)
             self.graphs.append(g)
 
     def replay(self, i):

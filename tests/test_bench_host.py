@@ -43,3 +43,29 @@ def test_stored_traffic_is_reported_only_for_a_matching_hash(tmp_path, monkeypat
     assert b.measured_traffic("attn_fwd", "abc", None) == 123
     assert b.measured_traffic("attn_fwd", "def", None) is None
     assert b.measured_traffic("attn_bwd", "abc", None) is None
+
+
+def test_replayed_decode_calls_never_find_their_kv_in_a_cache():
+    """Every decode workload as the default run replays it (3 warm-up + 20 timed replays): between two reads
+    of the same K/V bytes the run reads at least 1 GB of K/V (the copy's own call and every call between),
+    so none of it can still sit in the 256 MB Infinity Cache."""
+    import numpy as np
+    import workloads as wl
+    b = _bench()
+    for name in b.DECODE_LEGS:
+        c = wl.DECODE_CONFIGS[name]
+        lens = wl.draw_lengths(c.seed, c.batch, c.len_lo, c.len_hi)
+        call_bytes = b.decode_kv_bytes(np.asarray(lens), c.n_kv_heads, c.d)
+        set_bytes = 2 * c.batch * c.max_seqlen_k * c.n_kv_heads * c.d * 2
+        nsets = b.rotation_sets(set_bytes)
+        assert nsets * set_bytes >= b.ROTATION_BYTES
+        reps = b.CALLS_PER_REPLAY[name]
+        plan = b.replay_plan(nsets, reps, 23)
+        assert all(len(g) == reps and all(0 <= j < nsets for j in g) for g in plan)
+        calls = [j for i in range(23) for j in plan[i % len(plan)]]
+        last = {}
+        for n, j in enumerate(calls):
+            if j in last:
+                between = n - last[j] - 1
+                assert (1 + between) * call_bytes >= 1e9, (name, n, between)
+            last[j] = n
