@@ -69,3 +69,69 @@ def test_replayed_decode_calls_never_find_their_kv_in_a_cache():
                 between = n - last[j] - 1
                 assert (1 + between) * call_bytes >= 1e9, (name, n, between)
             last[j] = n
+
+
+def _counter_csv(path, counter, rows):
+    with open(path, "w") as f:
+        f.write("Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n")
+        for i, (name, value) in enumerate(rows):
+            f.write(f'{i + 1},"{name}",{counter},{value}\n')
+
+
+def _counter_run_dispatches():
+    """Kernel names of a --counter-run: a set-up copy, the 1 GiB calibration copy, then every leg."""
+    names = ["__amd_rocclr_copyBuffer", "__amd_rocclr_copyBuffer"]
+    for w in ("gqa-decode", "gqa-decode-small", "multi-token-decode", "long-context-decode"):
+        names.append("void attn::(anonymous namespace)::decode_stream<128, false, 1, false>(int)")
+        if w != "gqa-decode-small":  # the grouped kernel serves the small decode: no combine
+            names.append("void attn::(anonymous namespace)::combine_pieces<128, false, 1>(int)")
+    names += ["void attn::(anonymous namespace)::fwd_persist<128, false>(int)",
+              "void attn::(anonymous namespace)::bwd_pre<128>(int)",
+              "void attn::(anonymous namespace)::bwd_dkdv<128, false>(int)",
+              "void attn::(anonymous namespace)::bwd_dq<128, false>(int)"]
+    return names
+
+
+def test_counter_ingest_scales_each_launch_by_the_calibration_copy(tmp_path, monkeypatch):
+    b = _bench()
+    names = _counter_run_dispatches()
+    # FETCH_SIZE reads half of the copy's bytes (scale 2), WRITE_SIZE all of them (scale 1).
+    fetch = [10.0, 512.0 * 1024] + [float(i + 1) for i in range(len(names) - 2)]
+    write = [10.0, 1024.0 * 1024] + [float(100 + i) for i in range(len(names) - 2)]
+    _counter_csv(tmp_path / "f.csv", "FETCH_SIZE", list(zip(names, fetch)))
+    _counter_csv(tmp_path / "w.csv", "WRITE_SIZE", list(zip(names, write)))
+    monkeypatch.setattr(b, "COUNTERS", str(tmp_path / "out.json"))
+    b.ingest_counters(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"))
+    import json
+    out = json.load(open(tmp_path / "out.json"))
+    assert out["calibration"]["fetch_scale"] == 2.0 and out["calibration"]["write_scale"] == 1.0
+    # dispatch k after the calibration copy has FETCH k + 1 and WRITE 100 + k KiB
+    expect, k = {}, 0
+    for key, prefixes, _, _ in b.COUNTER_LEGS:
+        n = 1 if key == "attn_decode:gqa-decode-small" else len(prefixes)
+        expect[key] = sum((k + j + 1) * 1024 * 2 + (100 + k + j) * 1024 for j in range(n))
+        k += n
+    assert {key: out[key]["bytes_per_launch"] for key in expect} == expect
+    assert list(out["attn_decode:gqa-decode-small"]["kernels"]) == ["decode_stream<128, false, 1, false>"]
+    assert out["attn_bwd"]["source_hash"] == b.source_hash(b.BWD_SOURCES)
+
+
+def test_counter_ingest_rejects_a_run_out_of_order(tmp_path, monkeypatch):
+    b = _bench()
+    names = _counter_run_dispatches()
+    names[-1], names[-2] = names[-2], names[-1]  # bwd_dq before bwd_dkdv
+    rows = [(n, 1024.0) for n in names]
+    _counter_csv(tmp_path / "f.csv", "FETCH_SIZE", rows)
+    _counter_csv(tmp_path / "w.csv", "WRITE_SIZE", rows)
+    monkeypatch.setattr(b, "COUNTERS", str(tmp_path / "out.json"))
+    import pytest
+    with pytest.raises(SystemExit):
+        b.ingest_counters(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"))
+    assert not (tmp_path / "out.json").exists()
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    import subprocess, sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr and r.stdout == ""
