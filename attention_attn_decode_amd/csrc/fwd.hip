@@ -73,8 +73,9 @@ constexpr int kBMP = 256;  // query rows per work-group
 // phase still issues 32 MFMAs.
 template <int D> constexpr int kBlockKeys = D == 256 ? 32 : 64;
 
-// One 256-row query tile x (heaviest first: x / BH counts down the query
-// tiles, x % BH walks (sequence, head)) in the work-group's LDS block smem.
+// One 256-row query tile x (heaviest first: x / BH counts the query tiles
+// back from the sequence's end, x % BH walks (sequence, head)) in the
+// work-group's LDS block smem.
 template <int D, bool F16>
 __device__ __forceinline__ void
 fwd_tile(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
@@ -100,11 +101,10 @@ fwd_tile(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
   uint16_t *const ktile = smem;               // K slots
   uint16_t *const vtile = smem + NSLOT * KT;  // V slots
 
-  const int mb = n_mblocks - 1 - x / BH;  // heaviest query tile first
+  const int te = x / BH;  // query tile counted from the sequence's end: the heaviest first
   const int u = x % BH;
   const int b = u / Hq, h = u % Hq;
   const int gk = h / (Hq / Hkv);
-  const int q0 = mb * kBMP;
   // Rows of sequence b: dense batches are [B][S] blocks; a packed
   // variable-length batch gives each sequence's first row in cu_q / cu_k
   // (clamped to the packed totals, so any offsets stay inside the buffers).
@@ -116,11 +116,16 @@ fwd_tile(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const int c0 = min(max(cu_k[b], 0), total_k), c1 = min(max(cu_k[b + 1], c0), total_k);
     qbase = a0, Sq = a1 - a0, kbase = c0, Sk = c1 - c0;
     lse_base = (size_t)qbase, lse_hs = total_q;
-    if (q0 >= Sq) return;  // the whole work-group: this sequence has fewer query tiles
   } else {
     qbase = b * Sq, kbase = b * Sk;
     lse_base = (size_t)b * Hq * Sq, lse_hs = Sq;
   }
+  // Tiles are aligned to the sequence's end, so a length that is not a
+  // multiple of the tile leaves its partial tile first, where a causal mask
+  // gives it the fewest key blocks; its rows before row 0 are idle like rows
+  // past Sq.
+  const int q0 = Sq - kBMP * (te + 1);
+  if (q0 + kBMP <= 0) return;  // the whole work-group: this sequence has fewer query tiles
   // Wave index in a scalar register: every per-wave condition below (group,
   // key range, skipped blocks) is then a uniform branch, and the barriers
   // inside group-dependent code are passed by whole waves only.
@@ -142,15 +147,15 @@ fwd_tile(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
   const int nblk = (kend + BN - 1) / BN;
   const int bound = row_bound(qrow);
   // Blocks this wave computes: up to its last row inside the sequence; none
-  // when all its rows lie past Sq (the last tile of a sequence), whose
+  // when all its rows lie past Sq or before row 0 (a partial tile), whose
   // results are never stored (the wave still stages its share and meets
   // every barrier).
   const int wave_lo = row_bound(r0), wave_hi = row_bound(min(r0 + 31, Sq - 1));
-  const int nbw = r0 >= Sq ? 0 : min(nblk, (wave_hi + BN - 1) / BN);
+  const int nbw = r0 >= Sq || r0 + 31 < 0 ? 0 : min(nblk, (wave_hi + BN - 1) / BN);
 
   uint4 qop[KST];
   {
-    const bool ok = qrow < Sq;
+    const bool ok = qrow >= 0 && qrow < Sq;
     const uint16_t *qp = q + ((size_t)(qbase + (ok ? qrow : 0)) * Hq + h) * D;
 #pragma unroll
     for (int kk = 0; kk < KST; ++kk) qop[kk] = ok ? ldg16(qp + (2 * kk + hl) * 8) : make_uint4(0, 0, 0, 0);
@@ -501,7 +506,7 @@ fwd_tile(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
   }
 
   const float l_col = wave_xor_sum(l_run, 32);
-  if (qrow >= Sq) return;
+  if (qrow < 0 || qrow >= Sq) return;
   const float inv = l_col > 0.f ? 1.f / l_col : 0.f;
   uint16_t *dst = o + ((size_t)(qbase + qrow) * Hq + h) * D;
 #pragma unroll
