@@ -28,7 +28,9 @@ decode workload reports the same, prefill reports TFLOP/s over the exact
 causal FLOPs (4 d per visible query-key pair), the backward TFLOP/s counted,
 as the backward page does, as 2.5 times the forward FLOPs. After the timed
 steps, two measurement kernels of the library give the device's practical
-ceilings (a streaming read of 2 GiB, a bf16 MFMA loop with its clock), and the
+ceilings (a streaming read of 2 GiB, a bf16 MFMA loop with its clock; the
+streaming read also over exactly each decode workload's K/V bytes, which a
+decode call is compared with as `frac_of_bare_read`), and the
 fp64 CPU oracle is timed on the host (the full headline decode; a sample of
 the prefill).
 
@@ -341,7 +343,7 @@ class DecodeLeg:
     def replay(self, i):
         self.graphs[i % len(self.graphs)].replay()
 
-    def report(self, read_peak):
+    def report(self, read_peak, same_read_us=None):
         ms = self.ms
         mean = statistics.fmean(ms)
         thirds = [ms[k::3] for k in range(3)] if len(ms) >= 3 else [ms]
@@ -361,7 +363,32 @@ class DecodeLeg:
             r["us_mean_plain"] = round(statistics.fmean(self.ms_plain) * 1e3, 2)
         if read_peak:
             r["frac_of_measured_read"] = round(gbps / read_peak, 4)
+        if same_read_us:
+            r["bare_read_same_bytes_us"] = round(same_read_us, 2)
+            r["frac_of_bare_read"] = round(same_read_us / (mean * 1e3), 4)
         return r
+
+
+def same_size_read_us(aa, dev, stream, nbytes):
+    """Best time of the library's streaming-read kernel over exactly `nbytes` (8 back-to-back launches
+    over copies rotated as the decode workloads rotate theirs, one event pair; best over grids)."""
+    import torch
+    ncopies = min(8, max(2, -(-ROTATION_BYTES // nbytes))) if nbytes < 2 * ROTATION_BYTES else 1
+    bufs = [torch.empty(nbytes // 4, dtype=torch.int32, device=dev) for _ in range(ncopies)]
+    out = torch.empty(2048 * 256, dtype=torch.int32, device=dev)
+    best = float("inf")
+    for grid in (192, 256, 384, 512):
+        for rep in range(3):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ev[0].record(stream)
+            for r in range(8):
+                aa.probe_stream_read(bufs[r % ncopies], out, grid, stream)
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            if rep:
+                best = min(best, ev[0].elapsed_time(ev[1]) / 8 * 1e3)
+    del bufs, out
+    return best
 
 
 def measured_peaks(aa, dev, stream):
@@ -594,9 +621,10 @@ def main():
 
     peaks = None if args.no_peaks else measured_peaks(aa, dev, stream)
     read_peak = peaks["stream_read_GBps"] if peaks else None
+    same_read = {} if args.no_peaks else {leg.name: same_size_read_us(aa, dev, stream, leg.kv_bytes) for leg in legs}
     mfma_peak = peaks["mfma_bf16_TFLOPs"] if peaks else None
 
-    dec = head.report(read_peak)
+    dec = head.report(read_peak, same_read.get(head.name))
     dec_mean_ms = dec["us_mean"] * 1e-3
     dec_gbps = head.kv_bytes / (statistics.fmean(head.ms) * 1e-3) / 1e9
     B, sq, Hq, Hkv, d, S = head.shape
@@ -638,7 +666,7 @@ def main():
             "algorithmic_bytes_per_launch": head.kv_bytes,
             "avg_launch_ms": round(dec_mean_ms, 5),
         },
-        "decode": {w: leg.report(read_peak) for w, leg in zip(DECODE_LEGS, legs)},
+        "decode": {w: leg.report(read_peak, same_read.get(w)) for w, leg in zip(DECODE_LEGS, legs)},
         "measured_peaks": peaks,
         "timing": ("HIP graph replays: each workload's calls captured once (decode: calls_per_replay back-to-back "
                    "calls per replay, K/V rotated over >= 1 GiB of resident copies; prefill, backward, packed "
