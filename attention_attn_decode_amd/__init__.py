@@ -52,6 +52,12 @@ def lib() -> ctypes.CDLL:
         return _lib
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"libattn.so not built at {LIB_PATH}; run attention_attn_decode_amd.build.build()")
+    # torch carries its own copy of the HIP runtime under the same soname, but asks for it by a name that
+    # an already-loaded /opt/rocm runtime does not match. Loaded before torch, this library would pull in
+    # the system runtime and torch would then load its own beside it: two runtimes that share no devices,
+    # memory or streams, so every launch on torch's tensors fails. With torch loaded first, this library
+    # binds to torch's runtime.
+    import torch  # noqa: F401
     L = ctypes.CDLL(LIB_PATH)
     vp, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     L.attn_decode_plan.argtypes = [i32, i32, i32, i32, i32, i32, i32,

@@ -231,3 +231,20 @@ def test_probe_validation_before_any_device_work():
     assert L.attn_probe_mfma_bf16(p, 0, 10, p, None) == -1
     assert L.attn_probe_mfma_bf16(p, 4, 0, p, None) == -1
     assert L.attn_probe_mfma_bf16(None, 4, 10, p, None) == -1
+
+
+def test_one_hip_runtime_whatever_is_imported_first():
+    """Loading the library before torch must not leave two HIP runtimes in the process (torch ships its
+    own copy; with two, launches on torch's tensors fail)."""
+    import subprocess
+    import sys
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "import attention_attn_decode_amd as aa\n"
+            "aa.lib()\n"
+            "import torch\n"
+            "maps = open('/proc/self/maps').read()\n"
+            "print(len({l.split()[-1] for l in maps.splitlines() if 'libamdhip64' in l}))\n"
+            ) % os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert r.stdout.strip().splitlines()[-1] == "1"
