@@ -47,7 +47,7 @@ def _decode_cases(n, seed=901):
     return out
 
 
-@pytest.mark.parametrize("case", _decode_cases(24), ids=lambda c: f"dec{c[0]}")
+@pytest.mark.parametrize("case", _decode_cases(64), ids=lambda c: f"dec{c[0]}")
 def test_random_decode(aa, case):
     i, B, Hq, Hkv, d, sq, lens, ns, dtype = case
     torch = G.torch()
@@ -80,7 +80,7 @@ def _prefill_cases(n, seed=921, dims=(64, 128)):
     return out
 
 
-@pytest.mark.parametrize("case", _prefill_cases(12) + [(12 + c[0],) + c[1:] for c in _prefill_cases(6, seed=927, dims=(256,))],
+@pytest.mark.parametrize("case", _prefill_cases(32) + [(32 + c[0],) + c[1:] for c in _prefill_cases(12, seed=927, dims=(256,))],
                          ids=lambda c: f"fwd{c[0]}")
 def test_random_prefill(aa, case):
     i, B, Sq, Sk, Hq, Hkv, d, causal, dtype = case
@@ -102,7 +102,7 @@ def _grad_parity(got, ref, scale, u, tag):
     assert worst <= 1.0, f"{tag}: max err/bound = {worst:.3f}"
 
 
-@pytest.mark.parametrize("case", _prefill_cases(8, seed=941), ids=lambda c: f"bwd{c[0]}")
+@pytest.mark.parametrize("case", _prefill_cases(24, seed=941), ids=lambda c: f"bwd{c[0]}")
 def test_random_backward(aa, case):
     """Forward and backward on the same random shape (gradient bound as in the backward tests)."""
     i, B, Sq, Sk, Hq, Hkv, d, causal, dtype = case
@@ -139,7 +139,7 @@ def _varlen_cases(n, seed=971):
     return out
 
 
-@pytest.mark.parametrize("case", _varlen_cases(8), ids=lambda c: f"var{c[0]}")
+@pytest.mark.parametrize("case", _varlen_cases(24), ids=lambda c: f"var{c[0]}")
 def test_random_varlen_prefill(aa, case):
     i, lq, lk, Hq, Hkv, d, causal = case
     torch = G.torch()
