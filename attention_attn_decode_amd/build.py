@@ -13,6 +13,10 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libattn.so")
 SOURCES = ["api.hip", "decode.hip", "fwd.hip", "bwd.hip", "probe.hip"]
+# A plain C caller of the library (no Python in its process), run by the C-ABI GPU test.
+CAPI_SRC = os.path.join(ROOT, "tests", "capi", "attn_capi_check.c")
+CAPI_BIN = os.path.join(ROOT, "tests", "capi", "attn_capi_check")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 ARCH = "gfx950"
 
 # Packed fp32 VALU forms are disabled for every device compile.
@@ -55,7 +59,22 @@ def build(verbose: bool = False, extra_flags=()) -> str:
     tmp = LIB_PATH + ".tmp"
     _run([cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *[j[0] for j in jobs]])
     os.replace(tmp, LIB_PATH)
+    build_capi_check()
     return LIB_PATH
+
+
+def build_capi_check() -> str:
+    """Compile the C caller as C99 with the host C compiler against include/attn.h and the system HIP
+    runtime; it finds libattn.so through a run path relative to itself."""
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        raise RuntimeError("no C compiler found for the C-ABI check program")
+    tmp = CAPI_BIN + ".tmp"
+    _run([cc, "-std=c99", "-O2", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROCM, "include"),
+          "-I", INCLUDE, CAPI_SRC, "-o", tmp, "-L", PKG, "-l:libattn.so", "-L", os.path.join(ROCM, "lib"),
+          "-lamdhip64", "-Wl,-rpath,$ORIGIN/../../attention_attn_decode_amd", "-Wl,-rpath," + os.path.join(ROCM, "lib")])
+    os.replace(tmp, CAPI_BIN)
+    return CAPI_BIN
 
 
 if __name__ == "__main__":

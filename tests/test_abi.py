@@ -248,3 +248,17 @@ def test_one_hip_runtime_whatever_is_imported_first():
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stderr[-2000:]
     assert r.stdout.strip().splitlines()[-1] == "1"
+
+
+def test_c_caller_compiles_as_c99_without_warnings():
+    """The C-ABI check program (and with it include/attn.h) compiles as C99 with -Wall -Wextra -Werror."""
+    import shutil
+    import subprocess
+    from attention_attn_decode_amd import build as B
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    r = subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-fsyntax-only", "-D__HIP_PLATFORM_AMD__",
+                        "-I", os.path.join(B.ROCM, "include"), "-I", B.INCLUDE, B.CAPI_SRC],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr[-2000:]
