@@ -546,9 +546,14 @@ fwd_pp(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
 // tiles, in snake order (forward in even rounds, backward in odd ones), so
 // the heavy and light ends of consecutive rounds pair up on each CU. The
 // assignment is static: no counter, nothing to clear between calls. The
-// launcher takes it for dense batches at d = 128; a packed batch's empty
-// tiles would unbalance a static assignment, at d = 64 two dispatched
-// work-groups per CU are faster, and at d = 256 the loop state would spill.
+// launcher takes it at d = 128, dense or packed (a packed batch's list holds
+// only its non-empty tiles); at d = 64 two dispatched work-groups per CU are
+// faster, and at d = 256 the loop state would spill.
+//
+// Sequences a packed persistent launch takes (their tile counts are staged in
+// LDS); larger packed batches use one work-group per tile.
+constexpr int kPersistMaxSeq = 4096;
+
 template <int D, bool F16>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fwd_persist(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
@@ -556,20 +561,88 @@ fwd_persist(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
             const int *__restrict__ cu_q, const int *__restrict__ cu_k, int total_q, int total_k,
             int Sq, int Sk, int Hq, int Hkv, int causal, float scale_log2, int n_mblocks, int BH) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[kTileLds<D>];
-  const long long ntiles = (long long)n_mblocks * BH;
+  __shared__ int ntl[kPersistMaxSeq];  // packed: query tiles of each sequence
   const int G = gridDim.x, g = blockIdx.x;
+  // The next tile's prologue rewrites the LDS slots: every wave must be past
+  // its last LDS read and its direct loads must have landed (each wave waited
+  // for its own before leaving the tile). The tile's O and LSE stores need
+  // not complete first (the next tile reads other memory), so this is a bare
+  // barrier, not a release fence that would wait for them.
+  auto between_tiles = []() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+  if (cu_q == nullptr) {
+    const long long ntiles = (long long)n_mblocks * BH;
+    bool odd = false;
+    for (long long base = 0; base < ntiles; base += G, odd = !odd) {
+      const long long x = base + (odd ? G - 1 - g : g);
+      if (x < ntiles)
+        fwd_tile<D, F16>(q, k, v, o, lse, cu_q, cu_k, total_q, total_k, Sq, Sk, Hq, Hkv, causal, scale_log2,
+                         n_mblocks, BH, (int)x, smem);
+      between_tiles();
+    }
+    return;
+  }
+  // Packed batch: the non-empty tiles as one list, heaviest first (tile m
+  // from a sequence's start carries about m + 1 key blocks under a causal
+  // mask): level w = n_mblocks .. 1 holds tile ntl[b] - w (counted from the
+  // end) of every sequence b with at least w tiles, in sequence then head
+  // order. Work-groups take list positions in snake order as above, and each
+  // follows the list with a cursor (level w, sequence cb, head ch) that every
+  // wave advances identically from the tile counts, so the assignment is
+  // static and the same in every wave: no counter, no sort.
+  const int B = BH / Hq, lane = threadIdx.x & 63;
+  for (int b = threadIdx.x; b < B; b += blockDim.x) {
+    const int a0 = min(max(cu_q[b], 0), total_q), a1 = min(max(cu_q[b + 1], a0), total_q);
+    ntl[b] = min((a1 - a0 + kBMP - 1) / kBMP, n_mblocks);
+  }
+  __syncthreads();
+  long long ntiles = 0;
+  for (int b0 = 0; b0 < B; b0 += 64) {
+    int t = b0 + lane < B ? ntl[b0 + lane] : 0;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) t += __shfl_xor(t, m, 64);
+    ntiles += t;
+  }
+  ntiles *= Hq;
+  int w = n_mblocks, cb = 0, ch = 0;
+  auto next_valid = [&](int start) {
+    for (int b0 = start; b0 < B; b0 += 64) {
+      const unsigned long long m = __ballot(b0 + lane < B && ntl[b0 + lane] >= w);
+      if (m) return b0 + __ffsll((long long)m) - 1;
+    }
+    return B;
+  };
+  auto settle = [&]() {  // the first sequence at or after cb with a tile at level w, else the next level
+    while (w > 0) {
+      cb = next_valid(cb);
+      if (cb < B) return;
+      --w;
+      cb = 0;
+    }
+  };
+  settle();
+  long long cur = 0;
   bool odd = false;
   for (long long base = 0; base < ntiles; base += G, odd = !odd) {
     const long long x = base + (odd ? G - 1 - g : g);
-    if (x < ntiles)
-      fwd_tile<D, F16>(q, k, v, o, lse, cu_q, cu_k, total_q, total_k, Sq, Sk, Hq, Hkv, causal, scale_log2, n_mblocks,
-                       BH, (int)x, smem);
-    // The next tile's prologue rewrites the LDS slots: every wave must be
-    // past its last LDS read and its direct loads must have landed (each wave
-    // waited for its own before leaving the tile). The tile's O and LSE stores
-    // need not complete first (the next tile reads other memory), so this is
-    // a bare barrier, not a release fence that would wait for them.
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (x < ntiles) {
+      for (long long kk = x - cur; kk > 0;) {  // move the cursor forward to list position x
+        const int left = Hq - ch;
+        if (kk < left) {
+          ch += (int)kk;
+          break;
+        }
+        kk -= left;
+        ch = 0;
+        ++cb;
+        settle();
+      }
+      cur = x;
+      // The same in every lane (from LDS and wave-wide votes): held in a scalar register.
+      const int xt = __builtin_amdgcn_readfirstlane((ntl[cb] - w) * BH + cb * Hq + ch);
+      fwd_tile<D, F16>(q, k, v, o, lse, cu_q, cu_k, total_q, total_k, Sq, Sk, Hq, Hkv, causal, scale_log2,
+                       n_mblocks, BH, xt, smem);
+    }
+    between_tiles();
   }
 }
 
@@ -600,6 +673,10 @@ hipError_t launch_fwd(const void *q, const void *k, const void *v, void *o, floa
     const int nwg = ntiles < ncu ? ntiles : ncu;
     if (f16) run(fwd_persist<128, true>, nwg);
     else run(fwd_persist<128, false>, nwg);
+  } else if (d == 128 && batch <= kPersistMaxSeq) {
+    const int ncu = current_cus();
+    if (f16) run(fwd_persist<128, true>, ncu);
+    else run(fwd_persist<128, false>, ncu);
   } else if (d == 256) {  // the persistent form's loop state would spill at d = 256
     if (f16) run(fwd_pp<256, true>, ntiles);
     else run(fwd_pp<256, false>, ntiles);

@@ -721,7 +721,7 @@ def main():
         tf = fl / (var_mean * 1e-3) / 1e12
         result["varlen_prefill"] = {
             "bound": "mfma",
-            "kernel": "fwd_pp (packed offsets, one work-group per tile)",
+            "kernel": "fwd_persist (packed d = 128: one persistent work-group per CU over the non-empty tiles)",
             "ms_mean": round(var_mean, 5),
             "ms_median": round(statistics.median(var_ms), 5),
             "ms_mean_plain": round(statistics.fmean(plain_ms["varlen_prefill"]), 5),
