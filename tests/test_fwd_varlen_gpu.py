@@ -104,3 +104,27 @@ def test_varlen_f16(aa):
     O_ref, L_ref = oracle.attention_varlen(x.q, x.k, x.v, x.cu_q, x.cu_k, True, dtype="f16")
     o, lse = run_varlen(aa, x, True)
     G.assert_parity(o, lse, O_ref, L_ref, "varlen f16")
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_varlen_many_sequences_both_grids(aa, causal):
+    """At d = 128 a packed batch of up to 4096 sequences runs on the persistent grid (the sequences' tile counts
+    sit in LDS) and a larger one on one work-group per tile. 4097 short sequences, empty query and key ranges
+    among them, go against the oracle; their first 4096 alone must give the same rows bit for bit, since both
+    grids run the same tile code."""
+    rng = np.random.default_rng(4097)
+    n = 4097
+    lq = rng.integers(0, 40, n)
+    lk = lq + rng.integers(0, 9, n)
+    lq[::97] = 0
+    lk[5::131] = 0
+    Hq, Hkv, d = 2, 1, 128
+    x = wl.make_varlen(lq, lk, Hq, Hkv, d, seed=4097 + causal)
+    O_ref, L_ref = oracle.attention_varlen(x.q, x.k, x.v, x.cu_q, x.cu_k, causal)
+    o, lse = run_varlen(aa, x, causal)
+    G.assert_parity(o, lse, O_ref, L_ref, f"varlen 4097 sequences causal={causal}")
+    tq, tk = int(x.cu_q[n - 1]), int(x.cu_k[n - 1])
+    head = wl.VarlenInputs(x.q[:tq], x.k[:tk], x.v[:tk], x.cu_q[:n], x.cu_k[:n], x.meta, x.dtype)
+    o2, lse2 = run_varlen(aa, head, causal)
+    assert np.array_equal(o2, o[:tq]), "4096-sequence call differs from the 4097-sequence call"
+    assert np.array_equal(lse2, lse[:, :tq]), "4096-sequence LSE differs from the 4097-sequence call"
