@@ -51,8 +51,19 @@ namespace {
 // heads. Measured on MI355X (256 CUs): d = 64 streams best with one work-group
 // of four waves per CU (1024 workers); d = 128, whose sub-blocks keep twice the
 // bytes in flight per wave, best with 7/8 of that (896) - more concurrent
-// streams lower the achieved HBM bandwidth.
-int auto_workers(int d) { return d >= 128 ? 896 : 1024; }
+// streams lower the achieved HBM bandwidth - unless its pieces would be short:
+// below 32 sub-blocks (1024 keys) of capacity per piece at 896 workers, a wave's
+// time is its start-up and load latency rather than its share of the bandwidth,
+// and 1024 workers finish sooner (batch-1 GQA calls over 32k-128k keys).
+int auto_workers(int d, int batch, int n_kv_heads, int max_seqlen_k) {
+  if (d < 128) return 1024;
+  if (d == 128) {
+    const long long units = (long long)batch * ((max_seqlen_k + 31) / 32);  // capacity per KV head
+    const long long pieces896 = (896 + n_kv_heads - 1) / n_kv_heads;
+    if (units < 32 * pieces896) return 1024;
+  }
+  return 896;
+}
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -78,8 +89,8 @@ unsigned decode_cols(int n_q_heads, int n_kv_heads, int seqlen_q) {
   return (n_q_heads / n_kv_heads) * seqlen_q > 16 ? 32u : 16u;
 }
 
-int plan_pieces(int n_kv_heads, int d, int num_splits) {
-  const int w = auto_workers(d);
+int plan_pieces(int batch, int n_kv_heads, int d, int max_seqlen_k, int num_splits) {
+  const int w = auto_workers(d, batch, n_kv_heads, max_seqlen_k);
   int p = num_splits > 0 ? num_splits : (w + n_kv_heads - 1) / n_kv_heads;
   if (p > ATTN_MAX_PIECES) p = ATTN_MAX_PIECES;
   return p < 1 ? 1 : p;
@@ -102,7 +113,7 @@ int attn_decode_plan(int batch, int n_q_heads, int n_kv_heads, int d, int seqlen
   if (pieces == nullptr || min_piece == nullptr || num_splits < 0) return ATTN_ERR_INVALID;
   const int st = check_decode_shape(n_q_heads, n_kv_heads, d, seqlen_q, batch, max_seqlen_k);
   if (st != ATTN_OK) return st;
-  *pieces = plan_pieces(n_kv_heads, d, num_splits);
+  *pieces = plan_pieces(batch, n_kv_heads, d, max_seqlen_k, num_splits);
   *min_piece = ATTN_MIN_PIECE;
   return ATTN_OK;
 }
@@ -112,7 +123,7 @@ size_t attn_decode_workspace_size(int batch, int n_q_heads, int n_kv_heads, int 
   if (num_splits < 0 ||
       check_decode_shape(n_q_heads, n_kv_heads, d, seqlen_q, batch, max_seqlen_k) != ATTN_OK)
     return 0;
-  return workspace_bytes_for(batch, n_kv_heads, d, plan_pieces(n_kv_heads, d, num_splits),
+  return workspace_bytes_for(batch, n_kv_heads, d, plan_pieces(batch, n_kv_heads, d, max_seqlen_k, num_splits),
                              decode_cols(n_q_heads, n_kv_heads, seqlen_q));
 }
 
@@ -158,7 +169,7 @@ int decode_impl(const void *q, const void *k_cache, const void *v_cache, const i
     return ATTN_ERR_MISALIGNED;
   // Without a workspace, one piece per KV head: every sequence is finished by
   // the wave that streams it and no partial is stored.
-  const int pieces = workspace ? plan_pieces(n_kv_heads, d, num_splits) : 1;
+  const int pieces = workspace ? plan_pieces(batch, n_kv_heads, d, max_seqlen_k, num_splits) : 1;
   const unsigned cols = decode_cols(n_q_heads, n_kv_heads, seqlen_q);
   const size_t need = workspace_bytes_for(batch, n_kv_heads, d, pieces, cols);
   if (workspace_bytes < need) return ATTN_ERR_WORKSPACE;
@@ -356,7 +367,7 @@ int attn_decode_noalloc(const void *q, const void *k_cache, const void *v_cache,
   if (!q || !k_cache || !v_cache || !seqlens_k || !o || num_splits < 0) return ATTN_ERR_INVALID;
   const int st = check_decode_shape(n_q_heads, n_kv_heads, d, seqlen_q, batch, max_seqlen_k);
   if (st != ATTN_OK) return st;
-  const size_t need = workspace_bytes_for(batch, n_kv_heads, d, plan_pieces(n_kv_heads, d, num_splits),
+  const size_t need = workspace_bytes_for(batch, n_kv_heads, d, plan_pieces(batch, n_kv_heads, d, max_seqlen_k, num_splits),
                                           decode_cols(n_q_heads, n_kv_heads, seqlen_q));
   if (need > (size_t)ATTN_NOALLOC_SCRATCH_BYTES) return ATTN_ERR_TOO_LARGE;
   void *ws = device_scratch();

@@ -90,7 +90,10 @@ extern "C" {
  * number of pieces per KV head (num_splits = 0 asks for the automatic value,
  * ceil(W / n_kv_heads) with W = 1024 workers for d = 64 and 896 for d >= 128,
  * about one work-group of four waves per CU on a 256-CU part, as measured best
- * for HBM streaming; a positive value is honoured up to ATTN_MAX_PIECES) and
+ * for HBM streaming; at d = 128 W = 1024 also when the capacity per piece at
+ * 896 workers, batch * ceil(max_seqlen_k / 32) / ceil(896 / n_kv_heads), is
+ * under 32 sub-blocks of 32 keys, where short pieces are latency-bound; a
+ * positive value is honoured up to ATTN_MAX_PIECES) and
  * `min_piece`.
  * Host-only; touches no device. Returns ATTN_OK or an error code.
  */

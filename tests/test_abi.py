@@ -47,8 +47,16 @@ def test_status_strings_and_version():
     assert "gfx950" in aa.version()
 
 
-def _expected_pieces(Hkv, d, req):
-    n = req if req > 0 else math.ceil((896 if d >= 128 else 1024) / Hkv)  # 256 CUs
+def _expected_pieces(B, Hkv, d, S, req):
+    """The automatic plan for a 256-CU part: 1024 workers at d = 64, 896 at d >= 128, and 1024 at d = 128 when
+    a piece at 896 workers would hold fewer than 32 sub-blocks of 32 keys of capacity."""
+    if req > 0:
+        n = req
+    else:
+        workers = 1024 if d < 128 else 896
+        if d == 128 and B * math.ceil(S / 32) < 32 * math.ceil(896 / Hkv):
+            workers = 1024
+        n = math.ceil(workers / Hkv)
     return max(1, min(n, aa.ATTN_MAX_PIECES))
 
 
@@ -61,7 +69,7 @@ def test_decode_plan_and_workspace(shape, req):
     ensure_built()
     B, Hq, Hkv, d, sq, S = shape
     pieces, min_piece = aa.attn_decode_plan(B, Hq, Hkv, d, sq, S, req)
-    assert pieces == _expected_pieces(Hkv, d, req)
+    assert pieces == _expected_pieces(B, Hkv, d, S, req)
     assert min_piece == aa.ATTN_MIN_PIECE
     ws = aa.attn_decode_workspace_size(B, Hq, Hkv, sq, d, S, req)
     assert ws == (0 if pieces == 1 else Hkv * (pieces + B) * 16 * (d + 2) * 4 + (B + 1) * 8)
@@ -75,6 +83,21 @@ def test_auto_plans_of_the_five_workloads():
     assert aa.attn_decode_plan(4, 32, 8, 128, 1, 131072) == (112, 64)
 
 
+def test_auto_plan_short_pieces():
+    """d = 128 calls whose pieces would be short at 896 workers take 1024; d = 256 keeps 896."""
+    ensure_built()
+    assert aa.attn_decode_plan(1, 16, 2, 128, 1, 131072) == (512, 64)   # 4096 sub-blocks over 448 pieces
+    assert aa.attn_decode_plan(1, 16, 1, 128, 1, 131072) == (1024, 64)
+    assert aa.attn_decode_plan(32, 32, 1, 128, 1, 8192) == (1024, 64)  # MQA at the headline capacity
+    assert aa.attn_decode_plan(1, 16, 2, 256, 1, 131072) == (448, 64)
+    assert aa.attn_decode_plan(1, 16, 2, 64, 1, 131072) == (512, 64)
+    # the threshold: 32 sub-blocks per piece at 112 pieces per KV head is 3584 sub-blocks of capacity
+    assert aa.attn_decode_plan(14, 64, 8, 128, 1, 8192) == (112, 64)   # 3584: not below
+    assert aa.attn_decode_plan(13, 64, 8, 128, 1, 8192) == (128, 64)   # 3328
+    assert aa.attn_decode_plan(14, 64, 8, 128, 1, 8161) == (112, 64)   # ceil(8161 / 32) = 256: 3584
+    assert aa.attn_decode_plan(14, 64, 8, 128, 1, 8160) == (128, 64)   # 255 sub-blocks each: 3570
+
+
 def test_workspace_size_formula():
     ensure_built()
     assert aa.attn_decode_workspace_size(4, 32, 8, 1, 128, 131072) == 8 * (112 + 4) * 16 * 130 * 4 + 5 * 8
@@ -83,7 +106,8 @@ def test_workspace_size_formula():
     assert aa.attn_decode_workspace_size(1, 8, 1, 1, 64, 0) == 0
     assert aa.attn_decode_workspace_size(1, 8, 3, 1, 64, 10) == 0  # Hq % Hkv != 0
     # more than 16 packed rows: 32 columns per partial
-    assert aa.attn_decode_workspace_size(4, 32, 1, 1, 128, 131072) == 1 * (896 + 4) * 32 * 130 * 4 + 5 * 8
+    # 4 x 4096 sub-blocks of capacity over 896 pieces is under 32 per piece: 1024 pieces
+    assert aa.attn_decode_workspace_size(4, 32, 1, 1, 128, 131072) == 1 * (1024 + 4) * 32 * 130 * 4 + 5 * 8
     assert aa.attn_decode_workspace_size(2, 16, 2, 4, 64, 4096) == 2 * (512 + 2) * 32 * 66 * 4 + 3 * 8
     assert aa.attn_decode_workspace_size(3, 16, 1, 1, 256, 70000) == 1 * (896 + 3) * 16 * 258 * 4 + 4 * 8
 
