@@ -409,3 +409,13 @@ def test_grouped_shapes_against_oracle(aa, case):
         lens[: min(B, 4)] = [0, 1, 33, S][: min(B, 4)]
     x = wl.make_decode(B, Hq, Hkv, d, sq, S, lens, seed=seed)
     check(aa, x, f"grouped {case[:6]}")
+
+
+@pytest.mark.parametrize("hkv,sq", [(1, 2), (2, 4)])
+def test_batch1_long_cache_short_pieces(aa, hkv, sq):
+    """Batch-1 GQA decode over 131072 keys, 16 query heads, d = 128, several new tokens: the automatic plan
+    spreads the cache over 1024 workers of 4-8 sub-blocks each, and the combine merges 512-1024 partials per
+    KV head."""
+    x = wl.make_decode(1, 16, hkv, 128, sq, 131072, [131072], seed=9400 + hkv + sq)
+    assert aa.attn_decode_plan(1, 16, hkv, 128, sq, 131072)[0] == 1024 // hkv
+    check(aa, x, f"batch-1 L=131072 16:{hkv} sq={sq}")
